@@ -1,0 +1,396 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test fixes a value by a closed form, a brute-force enumeration, a
+textbook/library routine on a special case, or an invariant, chosen so that a
+plausible slip in the oracle (a dropped term, a sign, an index, a transposed
+operand) fails at least one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# router logits
+# --------------------------------------------------------------------------
+def test_logits_unit_vector_router_picks_input_columns():
+    # W_r rows are unit vectors e_e (d > E): logits are exactly x[:, :E]; a
+    # transposed router ([d, E] read as [E, d]) would not even have the shape.
+    T, d, E = 5, 12, 7
+    x = rng(1).standard_normal((T, d))
+    w = np.zeros((E, d))
+    w[np.arange(E), np.arange(E)] = 1.0
+    np.testing.assert_array_equal(O.router_logits(x, w), x[:, :E])
+
+
+def test_logits_permuted_unit_router_and_bias():
+    T, d, E = 4, 9, 5
+    x = rng(2).standard_normal((T, d))
+    cols = np.array([8, 0, 3, 6, 1])
+    w = np.zeros((E, d))
+    w[np.arange(E), cols] = 2.0
+    b = np.array([0.5, -1.0, 0.0, 3.0, -0.25])
+    np.testing.assert_array_equal(O.router_logits(x, w, b), 2.0 * x[:, cols] + b)
+    # zero router: the logits are the bias alone
+    np.testing.assert_array_equal(O.router_logits(x, np.zeros((E, d)), b), np.broadcast_to(b, (T, E)))
+
+
+def test_logits_widen_bf16_bits():
+    # 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25 in bf16
+    x = np.array([[0x3F80, 0xC000, 0x3E80]], dtype=np.uint16)
+    w = np.array([[0x3F80, 0x3F80, 0x3F80], [0x0000, 0x3F80, 0x0000]], dtype=np.uint16)
+    np.testing.assert_array_equal(O.router_logits(x, w), [[1.0 - 2.0 + 0.25, -2.0]])
+
+
+# --------------------------------------------------------------------------
+# top-k selection (the bit-exact part)
+# --------------------------------------------------------------------------
+def brute_force_topk_set(row, k):
+    """The k-subset with the largest logit sum (unique when logits are distinct)."""
+    best, best_sum = None, -math.inf
+    for sub in itertools.combinations(range(len(row)), k):
+        s = sum(row[e] for e in sub)
+        if s > best_sum:
+            best, best_sum = sub, s
+    return set(best)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_topk_matches_subset_enumeration(k):
+    g = rng(3)
+    for _ in range(60):
+        row = g.permutation(8).astype(np.float64) * 0.37 - 1.1  # distinct values
+        chosen = O.select_experts(row, k)
+        assert set(chosen) == brute_force_topk_set(row, k)
+        vals = [row[e] for e in chosen]
+        assert all(vals[i] > vals[i + 1] for i in range(k - 1)), "slots must be largest first"
+
+
+def test_topk_k1_is_argmax_lowest_id():
+    g = rng(4)
+    for _ in range(200):
+        row = g.integers(-3, 3, size=16).astype(np.float64)  # many ties
+        assert O.select_experts(row, 1) == [int(np.argmax(row))]  # numpy returns the first maximum
+
+
+def test_topk_k_equals_E_is_full_descending_sort_with_id_ties():
+    g = rng(5)
+    for _ in range(100):
+        row = g.integers(-4, 4, size=12).astype(np.float64)
+        order = np.lexsort((np.arange(12), -row))  # key 1: -value, key 2: id
+        assert O.select_experts(row, 12) == order.tolist()
+
+
+def test_topk_all_equal_gives_lowest_ids():
+    for E, k in [(8, 2), (64, 8), (64, 6), (256, 16)]:
+        assert O.select_experts(np.full(E, 0.3), k) == list(range(k))
+
+
+def test_topk_signed_zero_ties_and_infinities():
+    row = np.array([0.0, -0.0, -np.inf, np.inf, -0.0])
+    # +inf first, then the three zeros by id, then -inf
+    assert O.select_experts(row, 5) == [3, 0, 1, 4, 2]
+
+
+def test_topk_nan_ranks_last():
+    row = np.array([np.nan, -5.0, np.nan, -np.inf, 1.0])
+    assert O.select_experts(row, 3) == [4, 1, 3]
+    assert O.select_experts(row, 5) == [4, 1, 3, 0, 2]
+
+
+# --------------------------------------------------------------------------
+# gate weights
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("L,E", [(0.0, 8), (2.5, 8), (-1.0, 64), (7.0, 64)])
+def test_softmax_closed_form_one_hot_logit(L, E):
+    row = np.zeros(E)
+    row[3] = L
+    p = O.softmax_row(row)
+    den = math.exp(L) + (E - 1)
+    assert p[3] == pytest.approx(math.exp(L) / den, rel=1e-15)
+    for e in range(E):
+        if e != 3:
+            assert p[e] == pytest.approx(1.0 / den, rel=1e-15)
+
+
+def test_route_weights_closed_form_with_and_without_renormalisation():
+    E, L = 8, 1.5
+    logits = np.zeros((1, E))
+    logits[0, 5] = L
+    # without renormalisation the weights are the softmax probabilities
+    ids, w = O.route(logits, 2, renormalize=False)
+    assert ids.tolist() == [[5, 0]]
+    den = math.exp(L) + E - 1
+    np.testing.assert_allclose(w, [[math.exp(L) / den, 1.0 / den]], rtol=1e-15)
+    # with renormalisation over the two slots: e^L/(e^L+1), 1/(e^L+1)
+    ids, w = O.route(logits, 2, renormalize=True)
+    np.testing.assert_allclose(w, [[math.exp(L) / (math.exp(L) + 1), 1 / (math.exp(L) + 1)]], rtol=1e-15)
+
+
+def test_route_weights_invariants():
+    g = rng(6)
+    logits = g.standard_normal((50, 64)) * 2
+    _, w = O.route(logits, 8, renormalize=True)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
+    _, w2 = O.route(logits, 8, renormalize=False)
+    assert np.all(w2.sum(1) < 1.0) and np.all(w2 > 0)
+    assert np.all(np.diff(w2, axis=1) <= 0), "weights follow the slot (descending logit) order"
+    # k = E with renormalisation: the weights are the full softmax (a library routine)
+    from scipy.special import softmax
+    ids, w3 = O.route(logits[:5, :10], 10, renormalize=True)
+    for t in range(5):
+        np.testing.assert_allclose(w3[t], softmax(logits[t, :10])[ids[t]], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# permutation (the bit-exact part)
+# --------------------------------------------------------------------------
+def bucket_permutation(ids, E):
+    """Independent construction: walk the experts in order, collect rows in flat order."""
+    flat = ids.ravel().tolist()
+    perm = []
+    counts = []
+    for e in range(E):
+        rows = [f for f, v in enumerate(flat) if v == e]
+        counts.append(len(rows))
+        perm += rows
+    return counts, perm
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 8, 2), (37, 64, 8), (100, 64, 6), (5, 256, 16)])
+def test_permutation_matches_bucket_walk_and_invariants(T, E, k):
+    g = rng(T * 1000 + E + k)
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)])
+    counts, offsets, perm, inv = O.permute(ids, E)
+    c_ref, p_ref = bucket_permutation(ids, E)
+    assert counts.tolist() == c_ref
+    assert perm.tolist() == p_ref
+    assert offsets[0] == 0 and offsets[-1] == T * k and np.all(np.diff(offsets) == counts)
+    assert sorted(perm.tolist()) == list(range(T * k)), "perm is a bijection"
+    assert np.array_equal(inv[perm], np.arange(T * k))
+    flat = ids.ravel()
+    assert np.all(np.diff(flat[perm]) >= 0), "expert ids non-decreasing along perm"
+    tok = perm // k
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0), "flat index strictly increasing within a segment"
+        assert np.all(np.diff(tok[offsets[e]:offsets[e + 1]]) > 0)
+    # every token appears exactly k times
+    assert np.all(np.bincount(tok, minlength=T) == k)
+
+
+# --------------------------------------------------------------------------
+# expert FFN and the layer
+# --------------------------------------------------------------------------
+def silu_scalar(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def test_silu_closed_forms():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert O.silu(np.array([2.0]))[0] == pytest.approx(2.0 / (1.0 + math.exp(-2.0)), rel=1e-15)
+    assert O.silu(np.array([-2.0]))[0] == pytest.approx(-2.0 / (1.0 + math.exp(2.0)), rel=1e-15)
+    assert O.silu(np.array([40.0]))[0] == pytest.approx(40.0, rel=1e-15)
+    assert abs(O.silu(np.array([-40.0]))[0]) < 1e-15
+
+
+def probe_layer(E=3, d=6, I=4, S=0):
+    """Experts with one nonzero weight per matrix, at distinct positions.
+
+    Expert e: W_gate[e][ng, cg] = a, W_up[e][ng, cu] = b, W_down[e][m, ng] = c,
+    so FFN_e(x) = c * silu(a x[cg]) * (b x[cu]) in output m and 0 elsewhere.
+    Shapes are [I, d], [I, d], [d, I] with d != I, so a swapped index or a
+    transposed matrix moves or drops the value.
+    """
+    G = E + S
+    wg = np.zeros((G, I, d))
+    wu = np.zeros((G, I, d))
+    wd = np.zeros((G, d, I))
+    spec = []
+    for e in range(G):
+        ng, cg, cu, m = (e + 1) % I, (2 * e + 1) % d, (3 * e + 4) % d, (5 * e + 2) % d
+        a, b, c = 0.7 + 0.1 * e, -1.3 + 0.2 * e, 0.9 - 0.3 * e
+        wg[e, ng, cg], wu[e, ng, cu], wd[e, m, ng] = a, b, c
+        spec.append((ng, cg, cu, m, a, b, c))
+    return O.Experts(wg, wu, wd), spec
+
+
+def probe_output(spec, x_t, d):
+    ng, cg, cu, m, a, b, c = spec
+    y = np.zeros(d)
+    y[m] = c * silu_scalar(a * x_t[cg]) * (b * x_t[cu])
+    return y
+
+
+def test_layer_probe_experts_closed_form():
+    E, d, k = 3, 6, 2
+    ex, spec = probe_layer(E=E, d=d)
+    x = np.array([[1.5, -0.5, 2.0, 0.25, -1.25, 0.75],
+                  [-2.0, 1.0, -0.5, 3.0, 0.5, -1.0]])
+    ids = np.array([[2, 0], [1, 2]])
+    w = np.array([[0.6, 0.4], [0.25, 0.75]])
+    y = O.moe_layer(x, ex, ids, w, n_shared=0, n_experts=E)
+    for t in range(2):
+        ref = sum(w[t, j] * probe_output(spec[ids[t, j]], x[t], d) for j in range(k))
+        np.testing.assert_allclose(y[t], ref, rtol=1e-15, atol=0)
+
+
+def test_layer_probe_shared_experts_weight_one_after_routed():
+    E, S, d = 2, 2, 6
+    ex, spec = probe_layer(E=E, S=S, d=d)
+    x = np.array([[0.3, -1.0, 2.5, -0.75, 1.25, 0.5]])
+    ids = np.array([[1]])
+    w = np.array([[0.4]])
+    res = np.array([[10.0, 20.0, 30.0, 40.0, 50.0, 60.0]])
+    y = O.moe_layer(x, ex, ids, w, n_shared=S, n_experts=E, residual=res)
+    ref = 0.4 * probe_output(spec[1], x[0], d) + probe_output(spec[2], x[0], d) \
+        + probe_output(spec[3], x[0], d) + res[0]
+    np.testing.assert_allclose(y[0], ref, rtol=1e-15)
+
+
+def random_experts(G, d, I, seed, scale=0.3):
+    g = rng(seed)
+    return O.Experts(g.standard_normal((G, I, d)) * scale, g.standard_normal((G, I, d)) * scale,
+                     g.standard_normal((G, d, I)) * scale)
+
+
+def test_layer_single_expert_is_dense_swiglu():
+    # E = 1, k = 1: the weight is 1 (renormalised or not) and the layer is one SwiGLU FFN
+    d, I, T = 5, 7, 4
+    ex = random_experts(1, d, I, 7)
+    x = rng(8).standard_normal((T, d))
+    logits = rng(9).standard_normal((T, 1))
+    for ren in (False, True):
+        ids, w = O.route(logits, 1, ren)
+        np.testing.assert_array_equal(w, 1.0)
+        y = O.moe_layer(x, ex, ids, w, 0, 1)
+        wg, wu, wd = ex.get(0)
+        for t in range(T):
+            g_ = [sum(wg[n, c] * x[t, c] for c in range(d)) for n in range(I)]
+            u_ = [sum(wu[n, c] * x[t, c] for c in range(d)) for n in range(I)]
+            h_ = [silu_scalar(g_[n]) * u_[n] for n in range(I)]
+            o_ = [sum(wd[m, n] * h_[n] for n in range(I)) for m in range(d)]
+            np.testing.assert_allclose(y[t], o_, rtol=1e-12)
+
+
+def test_layer_zero_input_gives_residual():
+    E, d, I, T = 4, 6, 5, 3
+    ex = random_experts(E + 1, d, I, 10)
+    ids = np.array([[0, 3], [1, 2], [3, 1]])
+    w = np.full((T, 2), 0.5)
+    res = rng(11).standard_normal((T, d))
+    y = O.moe_layer(np.zeros((T, d)), ex, ids, w, 1, E, residual=res)
+    np.testing.assert_array_equal(y, res)
+
+
+def test_layer_power_of_two_scaling_is_exact():
+    E, d, I, T, S = 4, 6, 5, 3, 1
+    g = rng(12)
+    wg, wu, wd = g.standard_normal((E + S, I, d)), g.standard_normal((E + S, I, d)), g.standard_normal((E + S, d, I))
+    x = g.standard_normal((T, d))
+    ids = np.array([[0, 3], [1, 2], [3, 1]])
+    w = g.random((T, 2))
+    y1 = O.moe_layer(x, O.Experts(wg, wu, wd), ids, w, S, E)
+    y2 = O.moe_layer(x, O.Experts(wg, wu, 2 * wd), ids, w, S, E)
+    y3 = O.moe_layer(x, O.Experts(wg, 4 * wu, wd), ids, w, S, E)
+    np.testing.assert_array_equal(y2, 2 * y1)
+    np.testing.assert_array_equal(y3, 4 * y1)
+
+
+def test_shared_experts_equal_one_wider_expert():
+    # two shared SwiGLUs of width I equal one SwiGLU of width 2I (gate/up rows and
+    # down columns concatenated)
+    d, I, T = 6, 4, 3
+    g = rng(13)
+    wg, wu, wd = g.standard_normal((2, I, d)), g.standard_normal((2, I, d)), g.standard_normal((2, d, I))
+    x = g.standard_normal((T, d))
+    none_ids = np.zeros((T, 0), dtype=np.int64)
+    none_w = np.zeros((T, 0))
+    y2 = O.moe_layer(x, O.Experts(wg, wu, wd), none_ids, none_w, n_shared=2, n_experts=0)
+    wide = O.Experts(np.concatenate([wg[0], wg[1]])[None], np.concatenate([wu[0], wu[1]])[None],
+                     np.concatenate([wd[0], wd[1]], axis=1)[None])
+    y1 = O.moe_layer(x, wide, none_ids, none_w, n_shared=1, n_experts=0)
+    np.testing.assert_allclose(y2, y1, rtol=1e-13)
+
+
+def test_slot_loop_equals_dense_masked_gates():
+    E, d, I, T, k, S = 8, 16, 12, 20, 3, 2
+    ex = random_experts(E + S, d, I, 14)
+    g = rng(15)
+    x = g.standard_normal((T, d))
+    logits = g.standard_normal((T, E))
+    ids, w = O.route(logits, k, True)
+    res = g.standard_normal((T, d))
+    y_loop = O.moe_layer(x, ex, ids, w, S, E, residual=res)
+    y_dense = O.moe_layer_dense(x, ex, ids, w, S, E, residual=res)
+    np.testing.assert_allclose(y_loop, y_dense, rtol=1e-12, atol=1e-13)
+
+
+def test_identical_experts_renormalised_output_independent_of_routing():
+    E, d, I, T, k = 6, 8, 5, 7, 3
+    one = random_experts(1, d, I, 16)
+    wg, wu, wd = one.get(0)
+    ex = O.Experts(np.repeat(wg[None], E, 0), np.repeat(wu[None], E, 0), np.repeat(wd[None], E, 0))
+    x = rng(17).standard_normal((T, d))
+    outs = []
+    for s in range(3):
+        ids, w = O.route(rng(100 + s).standard_normal((T, E)), k, True)
+        outs.append(O.moe_layer(x, ex, ids, w, 0, E))
+    ref = O.moe_layer(x, one, np.zeros((T, 1), dtype=np.int64), np.ones((T, 1)), 0, 1)
+    for y in outs:
+        np.testing.assert_allclose(y, ref, rtol=1e-13)
+
+
+def test_sorted_rows_and_combine_reassemble_the_layer():
+    E, d, I, T, k, S = 5, 8, 6, 9, 2, 1
+    ex = random_experts(E + S, d, I, 18)
+    g = rng(19)
+    x = g.standard_normal((T, d))
+    ids, w = O.route(g.standard_normal((T, E)), k, False)
+    counts, offsets, perm, inv = O.permute(ids, E)
+    h, rows = O.sorted_rows(x, ex, ids, perm, S, E)
+    assert rows.shape == (T * k + S * T, d) and h.shape == (T * k + S * T, I)
+    y = O.combine(rows, inv, w, S)
+    np.testing.assert_allclose(y, O.moe_layer(x, ex, ids, w, S, E), rtol=1e-13)
+    # the rows of expert e are exactly the tokens routed to e, in ascending token order
+    for e in range(E):
+        toks = perm[offsets[e]:offsets[e + 1]] // k
+        for r, t in zip(range(offsets[e], offsets[e + 1]), toks):
+            o, _ = O.expert_ffn(x[t], *ex.get(e))
+            np.testing.assert_array_equal(rows[r], o)
+
+
+def test_int8_dequantisation_scales_output_channels():
+    q = np.zeros((1, 3, 4), dtype=np.int8)
+    q[0, 0, 1] = 127
+    q[0, 2, 3] = -5
+    s = np.array([[0.5, 2.0, 0.25]], dtype=np.float32)
+    w = O.dequantize(q, s)
+    ref = np.zeros((1, 3, 4))
+    ref[0, 0, 1] = 63.5
+    ref[0, 2, 3] = -1.25
+    np.testing.assert_array_equal(w, ref)
+
+
+# --------------------------------------------------------------------------
+# stacked workload glue
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("c", [0.01, 1.0, 3.0, 100.0])
+def test_rmsnorm_constant_input_closed_form(c):
+    eps = 1e-5
+    y = O.rmsnorm(np.full((2, 16), c), eps)
+    np.testing.assert_allclose(y, 1.0 / math.sqrt(1.0 + eps / (c * c)), rtol=1e-14)
+
+
+def test_rmsnorm_hand_example():
+    y = O.rmsnorm(np.array([[3.0, -4.0]]), 0.0)
+    # mean square = (9 + 16) / 2 = 12.5
+    np.testing.assert_allclose(y, [[3 / math.sqrt(12.5), -4 / math.sqrt(12.5)]], rtol=1e-15)
