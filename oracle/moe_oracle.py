@@ -323,6 +323,21 @@ def rmsnorm(h: np.ndarray, eps: float) -> np.ndarray:
     return hf / np.sqrt(np.mean(hf * hf, axis=-1, keepdims=True) + eps)
 
 
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of float64 values, returned as float64.
+
+    Rounds the float64 significand directly to 8 bits (no float32 step)."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)                     # a = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)  # rint: half to even
+
+
+def stack_layer_input(h: np.ndarray, eps: float) -> np.ndarray:
+    """Input of one layer of the stacked workload: RMSNorm of the residual stream,
+    stored in bf16 like every activation of a bf16 layer."""
+    return round_to_bf16(rmsnorm(h, eps))
+
+
 def full_route(x: np.ndarray, w_router: np.ndarray, bias, k: int, renormalize: bool):
     """Router logits, then top-k gating (steps 1-2 end to end)."""
     logits = router_logits(x, w_router, bias)

@@ -394,3 +394,17 @@ def test_rmsnorm_hand_example():
     y = O.rmsnorm(np.array([[3.0, -4.0]]), 0.0)
     # mean square = (9 + 16) / 2 = 12.5
     np.testing.assert_allclose(y, [[3 / math.sqrt(12.5), -4 / math.sqrt(12.5)]], rtol=1e-15)
+
+
+def test_round_to_bf16_ties_and_pattern():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even -> 1
+    assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: ties to even -> 1 + 2^-6
+    assert O.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+    assert O.round_to_bf16(np.array([-3.0]))[0] == -3.0
+    assert O.round_to_bf16(np.array([0.0]))[0] == 0.0
+    v = O.round_to_bf16(np.random.default_rng(0).standard_normal(1000))
+    # every result has at most 8 significant bits
+    m, _ = np.frexp(v)
+    assert np.all(m * 256 == np.rint(m * 256))
