@@ -1,0 +1,81 @@
+// Deterministic combine back to token order (switchyard hero "Bit-identical" and §02 "No
+// atomics"): every output element is owned by one thread, which reads the token's k routed
+// rows through inv_perm, then its shared-expert rows, then the residual, and sums them in
+// fp32 in exactly that order before a single rounding.  Loads and stores are 16 bytes per
+// lane, so the kernel streams rows at HBM rate.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+template <typename AT>
+__global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int S,
+                                                 const AT* __restrict__ rows,
+                                                 const int32_t* __restrict__ inv_perm,
+                                                 const float* __restrict__ w,
+                                                 const AT* residual, AT* y) {
+  constexpr int V = 16 / sizeof(AT);
+  const int t = blockIdx.x;
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * V;
+  if (c >= d) return;
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  auto add = [&](const AT* src, float wt, bool scaled) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    if (sizeof(AT) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_lo(u[i]), hi = bf16_hi(u[i]);
+        acc[2 * i] = scaled ? fmaf(wt, lo, acc[2 * i]) : acc[2 * i] + lo;
+        acc[2 * i + 1] = scaled ? fmaf(wt, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = __uint_as_float(u[i]);
+        acc[i] = scaled ? fmaf(wt, f, acc[i]) : acc[i] + f;
+      }
+    }
+  };
+  for (int j = 0; j < k; ++j) {
+    const int r = inv_perm[(size_t)t * k + j];
+    add(rows + (size_t)r * d + c, w[(size_t)t * k + j], true);
+  }
+  for (int s = 0; s < S; ++s) add(rows + ((size_t)T * k + (size_t)s * T + t) * d + c, 1.f, false);
+  if (residual) add(residual + (size_t)t * d + c, 1.f, false);
+  AT* dst = y + (size_t)t * d + c;
+  if (sizeof(AT) == 2) {
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(dst) = o;
+  } else {
+    *reinterpret_cast<uint4*>(dst) =
+        make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                   __float_as_uint(acc[3]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const LayerDims& L, int T, const void* rows, const int32_t* inv_perm,
+                          const float* topk_w, const void* residual, void* y, hipStream_t s) {
+  const int V = L.act == MOE_F32 ? 4 : 8;
+  const int per_block = 256 * V;
+  dim3 grid(T, (L.d + per_block - 1) / per_block);
+  LaunchTimer timer(MOE_KERNEL_COMBINE, s);
+  if (L.act == MOE_F32)
+    k_combine<float><<<grid, 256, 0, s>>>(T, L.d, L.k, L.S, (const float*)rows, inv_perm, topk_w,
+                                          (const float*)residual, (float*)y);
+  else
+    k_combine<uint16_t><<<grid, 256, 0, s>>>(T, L.d, L.k, L.S, (const uint16_t*)rows, inv_perm,
+                                             topk_w, (const uint16_t*)residual, (uint16_t*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,213 @@
+// Stable sort of the T*k (token, slot) rows by expert, with a block-wide prefix scan and no
+// atomics (the switchyard page sorts rows by expert this way, §02 "Route and sort").
+//
+// One workgroup of 16 wavefronts.  Wavefront w owns a contiguous range of flat rows, walked
+// 64 at a time.  Inside a step, lanes holding the same expert id find each other with eight
+// ballots (one per bit of the id); the lowest such lane is the group's leader and the rank
+// of a lane among its peers is a popcount of the lower peers.  Pass 1 builds a per-wavefront
+// histogram in LDS (only leaders write, and no two leaders share an address), a column scan
+// over wavefronts plus an exclusive scan over experts turns it into per-wavefront bases, and
+// pass 2 repeats the walk and scatters each row to base + rank.  Because wavefronts own
+// ascending ranges and lanes are ranked in order, rows of one expert keep ascending flat
+// index: the sort is stable and its result unique.
+//
+// The same kernel writes the launch plan of the grouped FFN: the ascending list of groups
+// that have rows (touched routed experts, then the shared experts) and, for the MFMA path,
+// the list of (group, first row) M-tiles.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPermWaves = 16;
+constexpr int kMaxGroups = 256 + 8;
+
+__device__ __forceinline__ uint64_t peer_mask(int key, bool valid) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+__global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, int tile_m,
+                                                  const int32_t* __restrict__ ids,
+                                                  int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm,
+                                                  int32_t* __restrict__ inv_perm,
+                                                  int32_t* __restrict__ plan) {
+  __shared__ int hist[kPermWaves][256];
+  __shared__ int cnt[kMaxGroups];
+  __shared__ int base[kMaxGroups];
+  __shared__ int touched[kMaxGroups];
+  __shared__ int tile_start[kMaxGroups + 1];
+  __shared__ int n_routed_touched;
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int N = T * k;
+  const int per_wave = ((N + kPermWaves * kWave - 1) / (kPermWaves * kWave)) * kWave;
+  const int begin = wave * per_wave, end = min(N, begin + per_wave);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int e = lane; e < 256; e += kWave) hist[wave][e] = 0;
+  __syncthreads();
+
+  // pass 1: per-wavefront histograms
+  for (int b0 = begin; b0 < end; b0 += kWave) {
+    const int f = b0 + lane;
+    const bool valid = f < end;
+    int key = valid ? ids[f] : 0;
+    key = ((unsigned)key < (unsigned)E) ? key : E - 1;
+    const uint64_t peers = peer_mask(key, valid);
+    const int leader = __ffsll((long long)peers) - 1;
+    if (valid && lane == leader) hist[wave][key] += __popcll(peers);
+  }
+  __syncthreads();
+
+  // column scan over wavefronts
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w][e];
+      hist[w][e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+
+  // exclusive scans over experts (row offsets, touched-list positions): wavefront 0,
+  // four experts per lane
+  if (wave == 0) {
+    int c[4], s = 0, sf = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? cnt[e] : 0;
+      s += c[i];
+      sf += c[i] > 0;
+    }
+    int incl = s, inclf = sf;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave), of = __shfl_up(inclf, off, kWave);
+      if (lane >= off) {
+        incl += o;
+        inclf += of;
+      }
+    }
+    int ex = incl - s, exf = inclf - sf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        base[e] = ex;
+        counts[e] = c[i];
+        offsets[e] = ex;
+        if (c[i] > 0) touched[exf++] = e;
+        ex += c[i];
+      }
+    }
+    if (lane == kWave - 1) n_routed_touched = inclf;
+    if (lane <= S) offsets[E + lane] = N + lane * T;
+  }
+  __syncthreads();
+
+  const int nrt = n_routed_touched;
+  const int n_groups = nrt + S;
+  if (tid < S) touched[nrt + tid] = E + tid;
+  // per-wavefront bases
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int b = base[e];
+    for (int w = 0; w < kPermWaves; ++w) hist[w][e] += b;
+  }
+  __syncthreads();
+
+  // pass 2: scatter
+  for (int b0 = begin; b0 < end; b0 += kWave) {
+    const int f = b0 + lane;
+    const bool valid = f < end;
+    int key = valid ? ids[f] : 0;
+    key = ((unsigned)key < (unsigned)E) ? key : E - 1;
+    const uint64_t peers = peer_mask(key, valid);
+    const int leader = __ffsll((long long)peers) - 1;
+    const int pos = hist[wave][key] + __popcll(peers & lt_mask);
+    if (valid) {
+      perm[pos] = f;
+      inv_perm[f] = pos;
+    }
+    if (valid && lane == leader) hist[wave][key] = hist[wave][key] + __popcll(peers);
+  }
+
+  // plan: touched groups and M-tiles
+  int32_t* tl = plan + kPlanHeader;
+  for (int i = tid; i < n_groups; i += blockDim.x) tl[i] = touched[i];
+  if (tile_m > 0) {
+    if (wave == 0) {
+      // exclusive scan of tiles per touched group, five groups per lane
+      int nt[5], s = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int p = 5 * lane + i;
+        int rows = 0;
+        if (p < n_groups) {
+          const int g = touched[p];
+          rows = g < E ? cnt[g] : T;
+        }
+        nt[i] = (rows + tile_m - 1) / tile_m;
+        s += nt[i];
+      }
+      int incl = s;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+      }
+      int ex = incl - s;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int p = 5 * lane + i;
+        if (p < kMaxGroups) tile_start[p] = ex;
+        ex += nt[i];
+      }
+      if (lane == kWave - 1) tile_start[kMaxGroups] = incl;
+    }
+    __syncthreads();
+    int32_t* tiles = tl + (E + S);
+    for (int p = tid; p < n_groups; p += blockDim.x) {
+      const int g = touched[p];
+      const int rows = g < E ? cnt[g] : T;
+      int o = tile_start[p];
+      for (int m0 = 0; m0 < rows; m0 += tile_m, ++o) {
+        tiles[2 * o] = g;
+        tiles[2 * o + 1] = m0;
+      }
+    }
+    if (tid == 0) plan[1] = tile_start[kMaxGroups];
+  } else if (tid == 0) {
+    plan[1] = 0;
+  }
+  if (tid == 0) {
+    plan[0] = n_groups;
+    plan[2] = tile_m;
+    plan[3] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* plan,
+                          int tile_m, hipStream_t s) {
+  LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
+  k_permute<<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, ids, counts, offsets, perm, inv_perm,
+                               plan);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,224 @@
+// Router logits, top-k gating and the RMSNorm prologue.
+//
+// Router: logits[t,e] = sum_c x[t,c] W_r[e,c] + b[e] with fp32 accumulation.  A block of four
+// wavefronts stages a few token rows in LDS and each wavefront streams whole W_r rows with
+// 16-byte loads; at decode sizes every wavefront owns one expert (many small blocks, so the
+// 256 KiB router matrix is read by many CUs at once), at prefill sizes a block owns all
+// experts for its tokens (the router matrix is then re-read from L2, not HBM).
+//
+// Top-k: one wavefront per token (the switchyard page routes each token in one warp, §02
+// "Route and sort").  Each lane holds up to four logits; the selection is a k-round wave
+// argmax over a 64-bit key (order-preserving fp32 bits, then the inverted expert id), so it
+// is exact and ties go to the lower id.  The softmax runs over all E logits.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRouteTB = 8;  // tokens per router block (upper bound)
+
+template <typename AT>
+__device__ __forceinline__ float dot_chunk(const uint4& w, const uint4& x);
+template <>
+__device__ __forceinline__ float dot_chunk<uint16_t>(const uint4& w, const uint4& x) {
+  float a = 0.f;
+  a = dot2_bf16(w.x, x.x, a);
+  a = dot2_bf16(w.y, x.y, a);
+  a = dot2_bf16(w.z, x.z, a);
+  a = dot2_bf16(w.w, x.w, a);
+  return a;
+}
+template <>
+__device__ __forceinline__ float dot_chunk<float>(const uint4& w, const uint4& x) {
+  float a = __uint_as_float(w.x) * __uint_as_float(x.x);
+  a = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), a);
+  a = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), a);
+  a = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), a);
+  return a;
+}
+
+// grid: (ceil(T / tb_max), ceil(E / (4 * epw))); block 256; dynamic LDS tb_max * d * sizeof(AT)
+template <typename AT>
+__global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int epw, int tb_max,
+                                                       const AT* __restrict__ x,
+                                                       const AT* __restrict__ w,
+                                                       const float* __restrict__ bias,
+                                                       float* __restrict__ logits) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int t0 = blockIdx.x * tb_max;
+  const int tb = min(tb_max, T - t0);
+  constexpr int V = 16 / sizeof(AT);  // elements per 16-byte chunk
+  const int row_chunks = d / V;
+  uint4* xs = reinterpret_cast<uint4*>(smem);
+  const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)t0 * d);
+  for (int i = threadIdx.x; i < tb * row_chunks; i += blockDim.x) xs[i] = xg[i];
+  __syncthreads();
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int e0 = (blockIdx.y * 4 + wave) * epw;
+  for (int ei = 0; ei < epw; ++ei) {
+    const int e = e0 + ei;
+    if (e >= E) break;
+    const uint4* wr = reinterpret_cast<const uint4*>(w + (size_t)e * d);
+    float acc[kRouteTB];
+#pragma unroll
+    for (int t = 0; t < kRouteTB; ++t) acc[t] = 0.f;
+    for (int c = lane; c < row_chunks; c += kWave) {
+      const uint4 wv = wr[c];
+#pragma unroll
+      for (int t = 0; t < kRouteTB; ++t)
+        if (t < tb) acc[t] += dot_chunk<AT>(wv, xs[t * row_chunks + c]);
+    }
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int t = 0; t < kRouteTB; ++t) {
+      if (t < tb) {
+        const float s = wave_sum(acc[t]);
+        if (lane == 0) logits[(size_t)(t0 + t) * E + e] = s + b;
+      }
+    }
+  }
+}
+
+// order-preserving map of fp32 onto uint32 (+0 and -0 equal, NaN lowest)
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  if (v != v) return 0u;
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kMaxK = 16;
+
+// grid: ceil(T / 4); block 256 (one wavefront per token)
+__global__ __launch_bounds__(256) void k_topk(int T, int E, int k, int renorm,
+                                              const float* __restrict__ logits,
+                                              int32_t* __restrict__ ids, float* __restrict__ wout) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* lrow = logits + (size_t)t * E;
+  float l[4];
+  uint64_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      l[i] = lrow[e];
+      key[i] = ((uint64_t)order_bits(l[i]) << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
+    } else {
+      l[i] = -INFINITY;
+      key[i] = 0;
+    }
+  }
+  // softmax over all E
+  float m = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
+  m = wave_max(m);
+  float z[4], zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = (lane + kWave * i < E) ? expf(l[i] - m) : 0.f;
+    zs += z[i];
+  }
+  const float zsum = wave_sum(zs);
+
+  int sel_id[kMaxK];
+  float sel_z[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+      best = wave_max_u64(best);
+      const int e = (int)(0xFFFFu - (uint32_t)(best & 0xFFFFu));
+      const int owner = e & (kWave - 1), slot = e >> 6;
+      float zmine = z[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) zmine = (slot == i) ? z[i] : zmine;
+      sel_z[j] = __shfl(zmine, owner, kWave);
+      sel_id[j] = e;
+      if (lane == owner) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i == slot) key[i] = 0;
+      }
+    }
+  }
+  float den = zsum;
+  if (renorm) {
+    den = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) den += sel_z[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k && lane == j) {
+      ids[(size_t)t * k + j] = sel_id[j];
+      wout[(size_t)t * k + j] = sel_z[j] / den;
+    }
+  }
+}
+
+// y = x / sqrt(mean(x^2) + eps), one block per token, fp32 sums in a fixed order
+template <typename AT>
+__global__ __launch_bounds__(256) void k_rmsnorm(int d, float eps, const AT* __restrict__ x,
+                                                 AT* __restrict__ y) {
+  __shared__ float part[4];
+  const int t = blockIdx.x;
+  const AT* xr = x + (size_t)t * d;
+  AT* yr = y + (size_t)t * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    const float v = Act<AT>::load(xr, c);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if (threadIdx.x % kWave == 0) part[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += blockDim.x) Act<AT>::store(yr, c, Act<AT>::load(xr, c) * inv);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, float eps,
+                          hipStream_t s) {
+  LaunchTimer timer(MOE_KERNEL_RMSNORM, s);
+  if (L.act == MOE_F32)
+    k_rmsnorm<float><<<T, 256, 0, s>>>(L.d, eps, (const float*)x, (float*)xn);
+  else
+    k_rmsnorm<uint16_t><<<T, 256, 0, s>>>(L.d, eps, (const uint16_t*)x, (uint16_t*)xn);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const LayerDims& L, int T, const void* x, const void* w_router,
+                                const float* bias, float* logits, hipStream_t s) {
+  const int esz = L.act == MOE_F32 ? 4 : 2;
+  int tb = kRouteTB;
+  while (tb > 1 && (size_t)tb * L.d * esz > 64 * 1024) tb >>= 1;
+  // decode sizes: one expert per wavefront, many blocks; otherwise all experts per block
+  const int epw = (T <= 64) ? 1 : (L.E + 3) / 4;
+  dim3 grid((T + tb - 1) / tb, (L.E + 4 * epw - 1) / (4 * epw));
+  const size_t lds = (size_t)tb * L.d * esz;
+  LaunchTimer timer(MOE_KERNEL_ROUTER, s);
+  if (L.act == MOE_F32)
+    k_router_logits<float><<<grid, 256, lds, s>>>(T, L.d, L.E, epw, tb, (const float*)x,
+                                                  (const float*)w_router, bias, logits);
+  else
+    k_router_logits<uint16_t><<<grid, 256, lds, s>>>(T, L.d, L.E, epw, tb, (const uint16_t*)x,
+                                                     (const uint16_t*)w_router, bias, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const LayerDims& L, int T, const float* logits, int32_t* ids, float* w,
+                       hipStream_t s) {
+  LaunchTimer timer(MOE_KERNEL_TOPK, s);
+  k_topk<<<(T + 3) / 4, 256, 0, s>>>(T, L.E, L.k, L.renorm, logits, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

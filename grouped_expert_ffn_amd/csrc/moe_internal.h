@@ -1,0 +1,150 @@
+// Internal declarations of libmoe: device helpers and kernel launchers.
+// Everything here is gfx950 (CDNA4, wave64) code; nothing is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// -------------------------------------------------------------------------------------
+// scalar conversions
+// -------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+// two floats -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 += a.lo*b.lo + a.hi*b.hi over packed bf16 pairs (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Activation element access for the two activation types.
+template <typename AT> struct Act;
+template <> struct Act<float> {
+  __device__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Act<uint16_t> {
+  __device__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// -------------------------------------------------------------------------------------
+// wave-level helpers
+// -------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// -------------------------------------------------------------------------------------
+// plan buffer written by the permute kernel (int32 words)
+// -------------------------------------------------------------------------------------
+//   [0] number of groups with rows (touched routed experts + shared experts)
+//   [1] number of M-tiles in the tile list
+//   [2] M-tile height the tile list was built for
+//   [3] reserved
+//   [4 .. 4+E+S)            touched group ids, ascending (routed first, then shared)
+//   [4+E+S .. + 2*max_tiles) tile list: (group, first row within the group)
+constexpr int kPlanHeader = 4;
+constexpr int kMinTileM = 16;
+inline size_t plan_max_tiles(int T, int k, int E, int S) {
+  const size_t N = (size_t)T * k;
+  return N / kMinTileM + (size_t)E + (size_t)S * ((T + kMinTileM - 1) / kMinTileM) + 1;
+}
+inline size_t plan_words(int T, int k, int E, int S) {
+  return kPlanHeader + (size_t)(E + S) + 2 * plan_max_tiles(T, k, E, S);
+}
+
+// -------------------------------------------------------------------------------------
+// launchers (each returns hipSuccess or the launch error)
+// -------------------------------------------------------------------------------------
+// Brackets one kernel launch with the caller's events when moe_time_next_launch armed it.
+class LaunchTimer {
+ public:
+  LaunchTimer(int kernel, hipStream_t s);
+  ~LaunchTimer();
+ private:
+  void* stop_;
+  hipStream_t s_;
+};
+
+struct LayerDims {
+  int d, E, k, I, S, renorm, act, wdt;
+};
+
+hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, float eps,
+                          hipStream_t s);
+hipError_t launch_router_logits(const LayerDims& L, int T, const void* x, const void* w_router,
+                                const float* bias, float* logits, hipStream_t s);
+hipError_t launch_topk(const LayerDims& L, int T, const float* logits, int32_t* ids, float* w,
+                       hipStream_t s);
+hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* plan,
+                          int tile_m, hipStream_t s);
+
+struct FfnArgs {
+  const void* x;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* plan;
+  void* h;
+  void* rows;
+};
+// M-tile height the grouped FFN will use for T tokens (0: GEMV path, no tile list needed).
+int ffn_tile_m(const LayerDims& L, int T);
+hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+int gemm_tile_m();
+
+hipError_t launch_combine(const LayerDims& L, int T, const void* rows, const int32_t* inv_perm,
+                          const float* topk_w, const void* residual, void* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,140 @@
+"""The C ABI on the host: the library loads, exports what include/moe.h declares, sizes
+workspaces, and refuses bad arguments before touching the GPU (no kernels run here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from grouped_expert_ffn_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return abi.lib()
+
+
+def test_library_exports_every_declared_function(L):
+    decl = declared_functions()
+    assert decl == set(abi.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)$", out, flags=re.M))
+    assert decl <= exported
+    for name in decl:
+        assert hasattr(L, name)
+
+
+def test_header_compiles_as_c():
+    res = subprocess.run(["gcc", "-x", "c", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-"],
+                         input=f'#include "{HEADER}"\nint main(void){{return 0;}}\n', text=True,
+                         capture_output=True)
+    assert res.returncode == 0, res.stderr
+
+
+def desc(**kw):
+    base = dict(d_model=2048, n_experts=64, top_k=8, d_ff=1024)
+    base.update(kw)
+    return abi.make_desc(**base)
+
+
+def test_status_strings(L):
+    assert abi.status_str(0) == "MOE_OK"
+    assert abi.status_str(-3) == "MOE_ERR_WORKSPACE"
+    assert L.moe_version() >= 100
+
+
+def test_workspace_sizes(L):
+    d = desc()
+    T = 64
+    ffn = abi.moe_workspace_bytes(d, T, abi.MOE_WS_GROUPED_FFN)
+    assert ffn >= T * 8 * 1024 * 2  # h: R x I bf16
+    fwd = abi.moe_workspace_bytes(d, T, abi.MOE_WS_FORWARD)
+    assert fwd > ffn + T * 8 * 2048 * 2  # plus rows
+    assert abi.moe_workspace_bytes(d, T, abi.MOE_WS_PERMUTE) > 0
+    # pre_norm adds the normalised input
+    assert abi.moe_workspace_bytes(desc(pre_norm=True), T, abi.MOE_WS_FORWARD) >= fwd + T * 2048 * 2
+    # monotone in T
+    assert abi.moe_workspace_bytes(d, 2 * T, abi.MOE_WS_FORWARD) > fwd
+    # invalid descriptor -> 0
+    assert abi.moe_workspace_bytes(desc(top_k=65), T, abi.MOE_WS_FORWARD) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), abi.MOE_ERR_INVALID),
+    (dict(top_k=65), abi.MOE_ERR_INVALID),
+    (dict(n_experts=0), abi.MOE_ERR_INVALID),
+    (dict(d_model=-8), abi.MOE_ERR_INVALID),
+    (dict(n_shared=-1), abi.MOE_ERR_INVALID),
+    (dict(n_experts=512), abi.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=17, n_experts=64), abi.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=2040), abi.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=abi.MOE_F32, w_dtype=abi.MOE_I8), abi.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=abi.MOE_I8), abi.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_descriptor_is_refused_before_any_launch(L, kw, status):
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_route(desc(**kw), 4, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == status
+    assert abi.last_error()
+
+
+def test_null_and_misaligned_pointers_are_refused(L):
+    d = desc()
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_route(d, 4, None, 0x1000, None, None, 0x1000, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == abi.MOE_ERR_INVALID and "x" in str(ei.value)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_combine(d, 4, 0x1000, 0x1008, 0x1000, None, 0x1000, stream=0)
+    assert ei.value.status == abi.MOE_ERR_INVALID and "aligned" in str(ei.value)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_route(d, -1, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == abi.MOE_ERR_INVALID
+
+
+def test_small_workspace_is_refused(L):
+    d = desc()
+    need = abi.moe_workspace_bytes(d, 8, abi.MOE_WS_FORWARD)
+    w = abi.make_weights(0x1000, 0x1000, 0x1000)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_forward(d, 8, 0x1000, 0x1000, None, w, None, 0x1000, None, None, 0x1000, need - 1,
+                        stream=0)
+    assert ei.value.status == abi.MOE_ERR_WORKSPACE
+    plan = abi.moe_workspace_bytes(d, 8, abi.MOE_WS_PERMUTE)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_permute(d, 8, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, plan - 1, stream=0)
+    assert ei.value.status == abi.MOE_ERR_WORKSPACE
+
+
+def test_int8_requires_scales(L):
+    d = desc(w_dtype=abi.MOE_I8)
+    w = abi.make_weights(0x1000, 0x1000, 0x1000)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_grouped_ffn(d, 8, 0x1000, w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 30,
+                            stream=0)
+    assert ei.value.status == abi.MOE_ERR_INVALID and "s_gate" in str(ei.value)
+
+
+def test_zero_tokens_is_a_no_op(L):
+    d = desc()
+    w = abi.make_weights(0x1000, 0x1000, 0x1000)
+    # nothing is enqueued for T == 0, so fake addresses are never dereferenced
+    abi.moe_route(d, 0, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 0x1000, stream=0)
+    abi.moe_permute(d, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 20, stream=0)
+    abi.moe_grouped_ffn(d, 0, 0x1000, w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 20, stream=0)
+    abi.moe_combine(d, 0, 0x1000, 0x1000, 0x1000, None, 0x1000, stream=0)
+    abi.moe_forward(d, 0, 0x1000, 0x1000, None, w, None, 0x1000, None, None, 0x1000, 1 << 20,
+                    stream=0)
+    assert abi.last_error() == ""
