@@ -231,8 +231,9 @@ template <int MODE, bool I8>
 hipError_t run_gemm(const GemmArgs& a, int max_tiles, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE, I8>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE, I8>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int n_blk = MODE == 0 ? BN / 2 : BN;

@@ -1,18 +1,27 @@
 // Grouped GEMV for decode sizes: every touched expert in one launch, weights streamed once.
 //
 // At decode sizes an expert sees one to a few rows, so the layer is bound by reading the
-// touched experts' weights from HBM (the switchyard page's decode kernel is "a grouped GEMV"
-// that streams expert weights, §02 "One launch for all experts").  The kernel is laid out
-// for that: blockIdx.x walks the touched groups of the launch plan, blockIdx.y a block of
-// NB output channels.  A group of LPC lanes owns one output channel and reads its weight row
-// in LPC*16-byte coalesced runs; the group's rows of activations (gathered through perm for
-// gate/up, contiguous h rows for down) sit in LDS and are re-read per weight chunk.  The
-// channel's partial sums are reduced across its LPC lanes by xor-shuffles, then the
-// epilogue applies the int8 scale, the SwiGLU (gate/up) and rounds to the activation type.
+// touched experts' weights from HBM (the switchyard page's decode path is a grouped GEMV that
+// streams the expert weights, §02 "One launch for all experts").  What decides the speed is
+// how many bytes each CU keeps in flight, so the kernel is built around that:
 //
-// Weight/activation types: f32 x f32 (fp32 FMA), bf16 x bf16 (v_dot2_f32_bf16), int8 x bf16
-// (int8 -> bf16 is exact for |q| <= 127, then v_dot2_f32_bf16; the per-channel scale
-// multiplies the fp32 sum once).
+//  * blockIdx.y walks the touched groups of the launch plan, blockIdx.x a block of NB
+//    output channels of that group's weight matrix (or matrices: gate and up together);
+//    consecutive blocks stream consecutive stretches of one matrix;
+//  * the K dimension is split across the block's four wavefronts; inside a wavefront,
+//    eight lanes own one channel and read its weight row in 128-byte coalesced runs;
+//  * every weight load of the block is issued at once into registers before any math
+//    (about 16 x 16 B per lane), so a block costs about one memory round trip and several
+//    blocks per CU overlap theirs; the weights then stay in registers while the group's
+//    activation rows are processed in chunks of up to MB rows staged in LDS;
+//  * partial sums are reduced over the 8 lanes with DPP moves and over the 4 wavefronts
+//    through LDS in a fixed order, so results are bit-reproducible;
+//  * the epilogue applies the int8 per-channel scale, the SwiGLU (gate/up) and the
+//    rounding to the activation type.
+//
+// Weight x activation types: f32 x f32 (fp32 FMA), bf16 x bf16 (v_dot2_f32_bf16), int8 x bf16
+// (int8 -> bf16 is exact for |q| <= 127, then v_dot2_f32_bf16; the scale multiplies the fp32
+// sum once per channel).
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,14 +38,15 @@ struct GemvArgs {
   const int32_t* perm;
   const int32_t* plan;
   void* out;        // [R, N]
-  int K, N, k, E, kc;  // kc: K columns staged in LDS at a time
+  int K, N, k, E;
+  int mb_max;       // rows staged per chunk (<= kMB)
 };
 
-constexpr int kLPC = 8;  // lanes per output channel
-constexpr int kMB = 8;   // rows per pass (<= kLPC)
+constexpr int kMB = 8;  // max rows per chunk
+constexpr int kWaves = 4;
 
 template <typename WT> struct WTraits;
-template <> struct WTraits<float> { static constexpr int V = 4; };     // per 16-byte load
+template <> struct WTraits<float> { static constexpr int V = 4; };  // weights per 16-byte load
 template <> struct WTraits<uint16_t> { static constexpr int V = 8; };
 template <> struct WTraits<int8_t> { static constexpr int V = 16; };
 
@@ -104,119 +114,174 @@ template <> struct Dot<uint16_t, int8_t> {
 };
 
 // MODE 0: h = silu(W0 x) * (W1 x);  MODE 1: out = W0 h
-// grid: (slots, ceil(N / NB)); block 256; dynamic LDS kMB * kc * sizeof(AT)
-template <int MODE, typename AT, typename WT>
+// CPG: channels per 8-lane group (NB = 8 * CPG channels per block);
+// MAXIT: K steps (8 lanes x 16 B) per wavefront per round.
+// grid: (ceil(N / NB), slots); block 256; dynamic LDS mb_max * ROUND * sizeof(AT).
+// blockIdx.x is dispatched fastest, so the blocks in flight read consecutive N-blocks of
+// one expert: one contiguous stretch of memory streamed in order (measured 25% faster
+// than spreading the blocks in flight over many experts at the same offset).
+template <int MODE, typename AT, typename WT, int CPG, int MAXIT>
 __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
-  constexpr int CPW = kWave / kLPC;  // channels per wavefront
-  constexpr int NB = 4 * CPW;        // channels per block
-  constexpr int V = WTraits<WT>::V;  // elements per lane step
-  constexpr int XB = V * (int)sizeof(AT);  // activation bytes per lane step
+  constexpr int NMAT = MODE == 0 ? 2 : 1;
+  constexpr int NB = 8 * CPG;
+  constexpr int V = WTraits<WT>::V;             // weights per 16-byte load
+  constexpr int STEP = 8 * V;                   // K elements per 8-lane step
+  constexpr int ROUND = kWaves * MAXIT * STEP;  // K elements per round
   typedef Dot<AT, WT> D;
   extern __shared__ __align__(16) unsigned char xs[];
+  __shared__ float red[kWaves][CPG][NMAT][kMB][8];
 
-  const int slot = blockIdx.x;
+  const int slot = blockIdx.y;
   if (slot >= a.plan[0]) return;
   const int g = a.plan[kPlanHeader + slot];
+  const int K = a.K, N = a.N;
+  const int n0 = blockIdx.x * NB;
   const int r0 = a.offsets[g];
   const int M = a.offsets[g + 1] - r0;
-  const int K = a.K, N = a.N;
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int q = lane % kLPC, ci = lane / kLPC;
-  const int n = blockIdx.y * NB + wave * CPW + ci;
-  const bool nvalid = n < N;
-  const size_t wrow = ((size_t)g * N + (nvalid ? n : N - 1)) * K;
-  const WT* w0 = reinterpret_cast<const WT*>(a.w0) + wrow;
-  const WT* w1 = MODE == 0 ? reinterpret_cast<const WT*>(a.w1) + wrow : nullptr;
+  const int q = lane % 8, lg = lane / 8;
   const AT* in = reinterpret_cast<const AT*>(a.in);
-  const int row_bytes = a.kc * (int)sizeof(AT);
+  const int rounds = (K + ROUND - 1) / ROUND;
+  const int row_bytes = ROUND * (int)sizeof(AT);
 
-  for (int m0 = 0; m0 < M; m0 += kMB) {
-    const int mb = min(kMB, M - m0);
-    float acc0[kMB], acc1[kMB];
+  // weight rows of this lane's channels (clamped into the matrix; results discarded)
+  const WT* wp[CPG][NMAT];
 #pragma unroll
-    for (int m = 0; m < kMB; ++m) acc0[m] = acc1[m] = 0.f;
+  for (int c = 0; c < CPG; ++c) {
+    const size_t row = ((size_t)g * N + min(n0 + c * 8 + lg, N - 1)) * K;
+    wp[c][0] = reinterpret_cast<const WT*>(a.w0) + row;
+    if (NMAT == 2) wp[c][NMAT - 1] = reinterpret_cast<const WT*>(a.w1) + row;
+  }
 
-    for (int k0 = 0; k0 < K; k0 += a.kc) {
-      const int kc = min(a.kc, K - k0);
-      // stage rows m0 .. m0+mb-1, columns k0 .. k0+kc-1 of the input into LDS
+  uint4 wbuf[CPG][NMAT][MAXIT];
+  float acc[CPG][NMAT][kMB];
+  for (int m0 = 0; m0 < M; m0 += a.mb_max) {
+    const int mb = min(a.mb_max, M - m0);
+#pragma unroll
+    for (int c = 0; c < CPG; ++c)
+#pragma unroll
+      for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+        for (int m = 0; m < kMB; ++m) acc[c][t][m] = 0.f;
+
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int k_round = rd * ROUND;
+      const int cols = min(ROUND, K - k_round);
+      const int steps = (cols + STEP - 1) / STEP;  // 8-lane steps in this round
+      const int spw = (steps + kWaves - 1) / kWaves;
+      const int s_lo = wave * spw, s_hi = min(steps, s_lo + spw);
+      // (1) weights -> registers, all loads in flight at once (kept for every row chunk
+      //     when one round covers K)
+      if (m0 == 0 || rounds > 1) {
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+          const int col = k_round + (s_lo + it) * STEP + q * V;
+          const bool ok = (s_lo + it < s_hi) && col < K;
+#pragma unroll
+          for (int c = 0; c < CPG; ++c)
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+              wbuf[c][t][it] = ok ? *reinterpret_cast<const uint4*>(wp[c][t] + col) : make_uint4(0, 0, 0, 0);
+        }
+      }
+      // (2) activation rows m0 .. m0+mb-1, columns of this round -> LDS
       __syncthreads();
-      const int chunks = kc * (int)sizeof(AT) / 16;
+      const int chunks = cols * (int)sizeof(AT) / 16;
       for (int i = threadIdx.x; i < mb * chunks; i += blockDim.x) {
-        const int m = i / chunks, c = i % chunks;
+        const int m = i / chunks, cc = i % chunks;
         const int r = r0 + m0 + m;
         size_t src_row;
         if (MODE == 0)
-          src_row = (g < a.E) ? (size_t)(a.perm[r] / a.k) : (size_t)(r - r0);
+          src_row = (g < a.E) ? (size_t)(a.perm[r] / a.k) : (size_t)(m0 + m);
         else
           src_row = (size_t)r;
-        const uint4* src = reinterpret_cast<const uint4*>(in + src_row * K + k0);
-        reinterpret_cast<uint4*>(xs + m * row_bytes)[c] = src[c];
+        reinterpret_cast<uint4*>(xs + m * row_bytes)[cc] =
+            reinterpret_cast<const uint4*>(in + src_row * K + k_round)[cc];
       }
       __syncthreads();
-
-#pragma unroll 4
-      for (int c = q * V; c < kc; c += kLPC * V) {
-        const typename D::W wa = D::prep(*reinterpret_cast<const uint4*>(w0 + k0 + c));
-        typename D::W wb;
-        if (MODE == 0) wb = D::prep(*reinterpret_cast<const uint4*>(w1 + k0 + c));
-        const unsigned char* xp = xs + c * (int)sizeof(AT);
+      // (3) math
 #pragma unroll
-        for (int m = 0; m < kMB; ++m) {
-          if (m < mb) {
-            acc0[m] = D::run(wa, xp + m * row_bytes, acc0[m]);
-            if (MODE == 0) acc1[m] = D::run(wb, xp + m * row_bytes, acc1[m]);
-          }
+      for (int it = 0; it < MAXIT; ++it) {
+        const int st = s_lo + it;
+        const int xcol = st * STEP + q * V;  // column within the round
+        if (st < s_hi && xcol < cols) {
+          const unsigned char* xp = xs + xcol * (int)sizeof(AT);
+#pragma unroll
+          for (int c = 0; c < CPG; ++c)
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t) {
+              const typename D::W w = D::prep(wbuf[c][t][it]);
+#pragma unroll
+              for (int m = 0; m < kMB; ++m)
+                if (m < mb) acc[c][t][m] = D::run(w, xp + m * row_bytes, acc[c][t][m]);
+            }
         }
       }
-      (void)XB;
     }
-    // reduce over the channel's lanes
+    // (4) reduce over the 8 lanes of each channel (DPP), then over the wavefronts (LDS,
+    //     fixed order), then the epilogue
 #pragma unroll
-    for (int m = 0; m < kMB; ++m) {
+    for (int c = 0; c < CPG; ++c)
 #pragma unroll
-      for (int off = kLPC / 2; off >= 1; off >>= 1) {
-        acc0[m] += __shfl_xor(acc0[m], off, kWave);
-        if (MODE == 0) acc1[m] += __shfl_xor(acc1[m], off, kWave);
-      }
-    }
-    // lane q of the channel's group writes row m0 + q
+      for (int t = 0; t < NMAT; ++t)
 #pragma unroll
-    for (int m = 0; m < kMB; ++m) {
-      if (nvalid && m < mb && q == m) {
-        float v0 = acc0[m];
-        const size_t o = (size_t)(r0 + m0 + m) * N + n;
-        if (MODE == 0) {
-          float v1 = acc1[m];
-          if (a.s0) {
-            v0 *= a.s0[(size_t)g * N + n];
-            v1 *= a.s1[(size_t)g * N + n];
+        for (int m = 0; m < kMB; ++m) {
+          const float v = sum8(acc[c][t][m]);
+          if (m == q) red[wave][c][t][m][lg] = v;
+        }
+    __syncthreads();
+    if (wave == 0 && q < mb) {
+      const int m = q;
+      const size_t orow = (size_t)(r0 + m0 + m) * N;
+#pragma unroll
+      for (int c = 0; c < CPG; ++c) {
+        const int n = n0 + c * 8 + lg;
+        if (n < N) {
+          float v[NMAT];
+#pragma unroll
+          for (int t = 0; t < NMAT; ++t)
+            v[t] = (red[0][c][t][m][lg] + red[1][c][t][m][lg]) + (red[2][c][t][m][lg] + red[3][c][t][m][lg]);
+          if (MODE == 0) {
+            float gv = v[0], uv = v[NMAT - 1];
+            if (a.s0) {
+              gv *= a.s0[(size_t)g * N + n];
+              uv *= a.s1[(size_t)g * N + n];
+            }
+            Act<AT>::store(reinterpret_cast<AT*>(a.out), orow + n, silu(gv) * uv);
+          } else {
+            float ov = v[0];
+            if (a.s0) ov *= a.s0[(size_t)g * N + n];
+            Act<AT>::store(reinterpret_cast<AT*>(a.out), orow + n, ov);
           }
-          Act<AT>::store(reinterpret_cast<AT*>(a.out), o, silu(v0) * v1);
-        } else {
-          if (a.s0) v0 *= a.s0[(size_t)g * N + n];
-          Act<AT>::store(reinterpret_cast<AT*>(a.out), o, v0);
         }
       }
     }
   }
 }
 
-template <int MODE, typename AT, typename WT>
+template <int MODE, typename AT, typename WT, int CPG, int MAXIT>
 hipError_t run_gemv(const GemvArgs& a, int slots, hipStream_t s) {
-  constexpr int NB = 4 * (kWave / kLPC);
-  dim3 grid(slots, (a.N + NB - 1) / NB);
-  const size_t lds = (size_t)kMB * a.kc * sizeof(AT);
+  constexpr int V = WTraits<WT>::V;
+  constexpr int ROUND = kWaves * MAXIT * 8 * V;
+  dim3 grid((a.N + 8 * CPG - 1) / (8 * CPG), slots);
+  const size_t lds = (size_t)a.mb_max * ROUND * sizeof(AT);
   LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-  k_gemv<MODE, AT, WT><<<grid, 256, lds, s>>>(a);
+  k_gemv<MODE, AT, WT, CPG, MAXIT><<<grid, 256, lds, s>>>(a);
   return hipGetLastError();
 }
 
-// K columns staged per pass: a multiple of the lane-group span that keeps LDS <= 32 KiB
-int stage_cols(int K, int esz, int span) {
-  int kc = (32 * 1024) / (kMB * esz);
-  kc = (kc / span) * span;
-  return kc >= K ? K : kc;
+// Pick MAXIT (K steps per wavefront) so one round covers K when possible, and CPG so a
+// lane issues about 16 weight loads per N-block.
+template <int MODE, typename AT, typename WT>
+hipError_t dispatch_gemv(const GemvArgs& a, int slots, hipStream_t s) {
+  constexpr int V = WTraits<WT>::V;
+  constexpr int NMAT = MODE == 0 ? 2 : 1;
+  const int steps = (a.K + 8 * V - 1) / (8 * V);
+  const int spw = (steps + kWaves - 1) / kWaves;
+  if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 8), 2>(a, slots, s);
+  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 2 : 4), 4>(a, slots, s);
+  return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8>(a, slots, s);
 }
 
 }  // namespace
@@ -229,9 +294,8 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.plan = f.plan;
   a.k = L.k;
   a.E = L.E;
+  a.mb_max = T < kMB ? T : kMB;  // no group holds more than T rows
   hipError_t err;
-  const int esz = L.act == MOE_F32 ? 4 : 2;
-  const int span = kLPC * (L.wdt == MOE_I8 ? 16 : (L.wdt == MOE_F32 ? 4 : 8));
 
   // gate/up + SwiGLU
   a.in = f.x;
@@ -242,13 +306,12 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.h;
   a.K = L.d;
   a.N = L.I;
-  a.kc = stage_cols(L.d, esz, span);
   if (L.act == MOE_F32)
-    err = run_gemv<0, float, float>(a, slots, s);
+    err = dispatch_gemv<0, float, float>(a, slots, s);
   else if (L.wdt == MOE_I8)
-    err = run_gemv<0, uint16_t, int8_t>(a, slots, s);
+    err = dispatch_gemv<0, uint16_t, int8_t>(a, slots, s);
   else
-    err = run_gemv<0, uint16_t, uint16_t>(a, slots, s);
+    err = dispatch_gemv<0, uint16_t, uint16_t>(a, slots, s);
   if (err != hipSuccess) return err;
 
   // down
@@ -260,13 +323,12 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.rows;
   a.K = L.I;
   a.N = L.d;
-  a.kc = stage_cols(L.I, esz, span);
   if (L.act == MOE_F32)
-    err = run_gemv<1, float, float>(a, slots, s);
+    err = dispatch_gemv<1, float, float>(a, slots, s);
   else if (L.wdt == MOE_I8)
-    err = run_gemv<1, uint16_t, int8_t>(a, slots, s);
+    err = dispatch_gemv<1, uint16_t, int8_t>(a, slots, s);
   else
-    err = run_gemv<1, uint16_t, uint16_t>(a, slots, s);
+    err = dispatch_gemv<1, uint16_t, uint16_t>(a, slots, s);
   return err;
 }
 

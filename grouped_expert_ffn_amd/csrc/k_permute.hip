@@ -15,6 +15,7 @@
 // that have rows (touched routed experts, then the shared experts) and, for the MFMA path,
 // the list of (group, first row) M-tiles.
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -22,6 +23,7 @@ namespace {
 
 constexpr int kPermWaves = 16;
 constexpr int kMaxGroups = 256 + 8;
+constexpr int kFusedMaxRows = 2048;  // T*k limit of the fused top-k + sort kernel
 
 __device__ __forceinline__ uint64_t peer_mask(int key, bool valid) {
   uint64_t peers = __ballot(valid);
@@ -34,8 +36,13 @@ __device__ __forceinline__ uint64_t peer_mask(int key, bool valid) {
   return peers;
 }
 
+// FUSED: the kernel first runs top-k on `logits` for every token (one wavefront per token),
+// writing ids/w to global memory and the ids to LDS, and then sorts from LDS.
+template <bool FUSED>
 __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, int tile_m,
-                                                  const int32_t* __restrict__ ids,
+                                                  const float* __restrict__ logits, int renorm,
+                                                  float* __restrict__ topk_w,
+                                                  int32_t* __restrict__ ids,
                                                   int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm,
@@ -47,6 +54,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
   __shared__ int touched[kMaxGroups];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int n_routed_touched;
+  __shared__ int keys_lds[FUSED ? kFusedMaxRows : 1];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int N = T * k;
@@ -55,13 +63,18 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   for (int e = lane; e < 256; e += kWave) hist[wave][e] = 0;
+  if (FUSED) {
+    for (int t = wave; t < T; t += kPermWaves)
+      topk_token(logits + (size_t)t * E, E, k, renorm, lane, ids, topk_w, t, keys_lds);
+  }
   __syncthreads();
+  auto key_of = [&](int f) { return FUSED ? keys_lds[f] : ids[f]; };
 
   // pass 1: per-wavefront histograms
   for (int b0 = begin; b0 < end; b0 += kWave) {
     const int f = b0 + lane;
     const bool valid = f < end;
-    int key = valid ? ids[f] : 0;
+    int key = valid ? key_of(f) : 0;
     key = ((unsigned)key < (unsigned)E) ? key : E - 1;
     const uint64_t peers = peer_mask(key, valid);
     const int leader = __ffsll((long long)peers) - 1;
@@ -132,7 +145,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
   for (int b0 = begin; b0 < end; b0 += kWave) {
     const int f = b0 + lane;
     const bool valid = f < end;
-    int key = valid ? ids[f] : 0;
+    int key = valid ? key_of(f) : 0;
     key = ((unsigned)key < (unsigned)E) ? key : E - 1;
     const uint64_t peers = peer_mask(key, valid);
     const int leader = __ffsll((long long)peers) - 1;
@@ -205,8 +218,20 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* plan,
                           int tile_m, hipStream_t s) {
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
-  k_permute<<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, ids, counts, offsets, perm, inv_perm,
-                               plan);
+  k_permute<false><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr,
+                                      const_cast<int32_t*>(ids), counts, offsets, perm, inv_perm,
+                                      plan);
+  return hipGetLastError();
+}
+
+bool topk_permute_fusable(const LayerDims& L, int T) { return (size_t)T * L.k <= kFusedMaxRows; }
+
+hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, int32_t* ids,
+                               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_perm, int32_t* plan, int tile_m, hipStream_t s) {
+  LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
+  k_permute<true><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, logits, L.renorm, topk_w, ids,
+                                     counts, offsets, perm, inv_perm, plan);
   return hipGetLastError();
 }
 

@@ -1,22 +1,26 @@
 // Router logits, top-k gating and the RMSNorm prologue.
 //
 // Router: logits[t,e] = sum_c x[t,c] W_r[e,c] + b[e] with fp32 accumulation.  A block of four
-// wavefronts stages a few token rows in LDS and each wavefront streams whole W_r rows with
-// 16-byte loads; at decode sizes every wavefront owns one expert (many small blocks, so the
-// 256 KiB router matrix is read by many CUs at once), at prefill sizes a block owns all
-// experts for its tokens (the router matrix is then re-read from L2, not HBM).
+// wavefronts stages a few token rows in LDS; each wavefront first issues the loads of a whole
+// W_r row (16 bytes per lane per load, all in flight together), then reduces with DPP.  At
+// decode sizes every wavefront owns one expert (many small blocks, so the router matrix is
+// read by many CUs at once); at prefill sizes a block owns all experts for its tokens and
+// prefetches the next expert's row while reducing the current one.
 //
 // Top-k: one wavefront per token (the switchyard page routes each token in one warp, §02
-// "Route and sort").  Each lane holds up to four logits; the selection is a k-round wave
-// argmax over a 64-bit key (order-preserving fp32 bits, then the inverted expert id), so it
-// is exact and ties go to the lower id.  The softmax runs over all E logits.
+// "Route and sort").  Each lane holds up to four logits as 64-bit keys (order-preserving fp32
+// bits above the inverted expert id, so keys are distinct and ties go to the lower id); the
+// rank of every key is counted against all others broadcast by readlane, and the keys of rank
+// < k are the slots, largest first.  The softmax runs over all E logits; sums and the max use
+// DPP trees in a fixed order.
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
-namespace {
-
 constexpr int kRouteTB = 8;  // tokens per router block (upper bound)
+
+namespace {
 
 template <typename AT>
 __device__ __forceinline__ float dot_chunk(const uint4& w, const uint4& x);
@@ -46,50 +50,63 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
                                                        const float* __restrict__ bias,
                                                        float* __restrict__ logits) {
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int R = 8;                // 16-byte chunks per lane kept in flight
+  constexpr int V = 16 / sizeof(AT);  // elements per 16-byte chunk
   const int t0 = blockIdx.x * tb_max;
   const int tb = min(tb_max, T - t0);
-  constexpr int V = 16 / sizeof(AT);  // elements per 16-byte chunk
   const int row_chunks = d / V;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int e0 = (blockIdx.y * 4 + wave) * epw;
+
+  uint4 wv[R];
+  auto load_slice = [&](int e, int c0) {
+    const uint4* wr = reinterpret_cast<const uint4*>(w + (size_t)min(e, E - 1) * d);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int c = c0 + lane + kWave * i;
+      wv[i] = c < row_chunks ? wr[c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_slice(e0, 0);  // in flight while the activations are staged
+
   uint4* xs = reinterpret_cast<uint4*>(smem);
   const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)t0 * d);
   for (int i = threadIdx.x; i < tb * row_chunks; i += blockDim.x) xs[i] = xg[i];
   __syncthreads();
 
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int e0 = (blockIdx.y * 4 + wave) * epw;
   for (int ei = 0; ei < epw; ++ei) {
     const int e = e0 + ei;
     if (e >= E) break;
-    const uint4* wr = reinterpret_cast<const uint4*>(w + (size_t)e * d);
     float acc[kRouteTB];
 #pragma unroll
     for (int t = 0; t < kRouteTB; ++t) acc[t] = 0.f;
-    for (int c = lane; c < row_chunks; c += kWave) {
-      const uint4 wv = wr[c];
+    for (int c0 = 0; c0 < row_chunks; c0 += kWave * R) {
+      if (c0 > 0) load_slice(e, c0);
 #pragma unroll
-      for (int t = 0; t < kRouteTB; ++t)
-        if (t < tb) acc[t] += dot_chunk<AT>(wv, xs[t * row_chunks + c]);
+      for (int i = 0; i < R; ++i) {
+        const int c = c0 + lane + kWave * i;
+        if (c < row_chunks) {
+#pragma unroll
+          for (int t = 0; t < kRouteTB; ++t)
+            if (t < tb) acc[t] += dot_chunk<AT>(wv[i], xs[t * row_chunks + c]);
+        }
+      }
     }
+    if (ei + 1 < epw && e + 1 < E) load_slice(e + 1, 0);  // next expert's row
     const float b = bias ? bias[e] : 0.f;
 #pragma unroll
     for (int t = 0; t < kRouteTB; ++t) {
       if (t < tb) {
-        const float s = wave_sum(acc[t]);
-        if (lane == 0) logits[(size_t)(t0 + t) * E + e] = s + b;
+        const float sum = wave_sum_u(acc[t]);
+        if (lane == 0) logits[(size_t)(t0 + t) * E + e] = sum + b;
       }
     }
   }
 }
 
-// order-preserving map of fp32 onto uint32 (+0 and -0 equal, NaN lowest)
-__device__ __forceinline__ uint32_t order_bits(float v) {
-  if (v != v) return 0u;
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+}  // namespace
 
-constexpr int kMaxK = 16;
+namespace {
 
 // grid: ceil(T / 4); block 256 (one wavefront per token)
 __global__ __launch_bounds__(256) void k_topk(int T, int E, int k, int renorm,
@@ -98,68 +115,7 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int k, int renorm,
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  const float* lrow = logits + (size_t)t * E;
-  float l[4];
-  uint64_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) {
-      l[i] = lrow[e];
-      key[i] = ((uint64_t)order_bits(l[i]) << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
-    } else {
-      l[i] = -INFINITY;
-      key[i] = 0;
-    }
-  }
-  // softmax over all E
-  float m = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
-  m = wave_max(m);
-  float z[4], zs = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    z[i] = (lane + kWave * i < E) ? expf(l[i] - m) : 0.f;
-    zs += z[i];
-  }
-  const float zsum = wave_sum(zs);
-
-  int sel_id[kMaxK];
-  float sel_z[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xFFFFu - (uint32_t)(best & 0xFFFFu));
-      const int owner = e & (kWave - 1), slot = e >> 6;
-      float zmine = z[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) zmine = (slot == i) ? z[i] : zmine;
-      sel_z[j] = __shfl(zmine, owner, kWave);
-      sel_id[j] = e;
-      if (lane == owner) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i == slot) key[i] = 0;
-      }
-    }
-  }
-  float den = zsum;
-  if (renorm) {
-    den = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) den += sel_z[j];
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k && lane == j) {
-      ids[(size_t)t * k + j] = sel_id[j];
-      wout[(size_t)t * k + j] = sel_z[j] / den;
-    }
-  }
+  topk_token(logits + (size_t)t * E, E, k, renorm, lane, ids, wout, t, nullptr);
 }
 
 // y = x / sqrt(mean(x^2) + eps), one block per token, fp32 sums in a fixed order
@@ -175,7 +131,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(int d, float eps, const AT* __r
     const float v = Act<AT>::load(xr, c);
     ss = fmaf(v, v, ss);
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_u(ss);
   if (threadIdx.x % kWave == 0) part[threadIdx.x / kWave] = ss;
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);

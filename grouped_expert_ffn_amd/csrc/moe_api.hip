@@ -132,13 +132,13 @@ int32_t check_weights(const LayerDims& L, const moe_expert_weights_t* w) {
 
 LaunchTimer::LaunchTimer(int kernel, hipStream_t s) : stop_(nullptr), s_(s) {
   if (kernel >= 0 && kernel < MOE_KERNEL_COUNT && g_timer_start[kernel]) {
-    hipEventRecord((hipEvent_t)g_timer_start[kernel], s);
+    (void)hipEventRecord((hipEvent_t)g_timer_start[kernel], s);
     stop_ = g_timer_stop[kernel];
     g_timer_start[kernel] = g_timer_stop[kernel] = nullptr;
   }
 }
 LaunchTimer::~LaunchTimer() {
-  if (stop_) hipEventRecord((hipEvent_t)stop_, s_);
+  if (stop_) (void)hipEventRecord((hipEvent_t)stop_, s_);
 }
 
 int ffn_tile_m(const LayerDims& L, int T) {
@@ -334,10 +334,16 @@ int32_t moe_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, cons
   int32_t* plan = (int32_t*)(base + f.plan);
   if ((e = launch_router_logits(L, T, xin, w_router, router_bias, logits, s)) != hipSuccess)
     return device_fail(e, "router logits launch");
-  if ((e = launch_topk(L, T, logits, ids, w, s)) != hipSuccess) return device_fail(e, "top-k launch");
-  if ((e = launch_permute(L, T, ids, counts, offsets, perm, inv_perm, plan, ffn_tile_m(L, T), s)) !=
-      hipSuccess)
-    return device_fail(e, "permute launch");
+  if (topk_permute_fusable(L, T)) {
+    if ((e = launch_topk_permute(L, T, logits, ids, w, counts, offsets, perm, inv_perm, plan,
+                                 ffn_tile_m(L, T), s)) != hipSuccess)
+      return device_fail(e, "top-k + permute launch");
+  } else {
+    if ((e = launch_topk(L, T, logits, ids, w, s)) != hipSuccess) return device_fail(e, "top-k launch");
+    if ((e = launch_permute(L, T, ids, counts, offsets, perm, inv_perm, plan, ffn_tile_m(L, T), s)) !=
+        hipSuccess)
+      return device_fail(e, "permute launch");
+  }
   FfnArgs a{xin, weights->w_gate, weights->w_up, weights->w_down, weights->s_gate, weights->s_up,
             weights->s_down, offsets, perm, plan, base + f.h, base + f.rows};
   if (L.wdt != MOE_I8) a.s_gate = a.s_up = a.s_down = nullptr;

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -58,6 +58,46 @@ template <> struct Act<uint16_t> {
 // -------------------------------------------------------------------------------------
 // wave-level helpers
 // -------------------------------------------------------------------------------------
+// DPP lane moves (VALU modifiers, no LDS round trip).  Controls: quad_perm [1,0,3,2] = 0xB1,
+// quad_perm [2,3,0,1] = 0x4E, row_half_mirror (lane i <-> 7-i within 8) = 0x141,
+// row_mirror (lane i <-> 15-i within 16) = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+// Sum over each aligned group of 8 lanes; every lane of the group gets the same bits
+// (each step adds a value and its partner, and fp addition is commutative).
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Wave-wide sum / max, identical (wave-uniform) in every lane, fixed order.
+__device__ __forceinline__ float wave_sum_u(float v) {
+  v = sum16(v);
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+__device__ __forceinline__ float wave_max_u(float v) {
+  v = max16(v);
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -122,6 +162,12 @@ hipError_t launch_topk(const LayerDims& L, int T, const float* logits, int32_t* 
 hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* plan,
                           int tile_m, hipStream_t s);
+
+// Top-k and the sort fused in one workgroup (small T*k only; see topk_permute_fusable).
+bool topk_permute_fusable(const LayerDims& L, int T);
+hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, int32_t* ids,
+                               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_perm, int32_t* plan, int tile_m, hipStream_t s);
 
 struct FfnArgs {
   const void* x;
