@@ -1,8 +1,9 @@
-// Deterministic combine back to token order (switchyard hero "Bit-identical" and §02 "No
-// atomics"): every output element is owned by one thread, which reads the token's k routed
-// rows through inv_perm, then its shared-expert rows, then the residual, and sums them in
-// fp32 in exactly that order before a single rounding.  Loads and stores are 16 bytes per
-// lane, so the kernel streams rows at HBM rate.
+// Deterministic combine back to token order (switchyard page, hero statistics: expert-
+// parallel output equal to one GPU bit for bit; §02 "Kernels and dispatch": no atomics).
+// Every output element is owned by one thread, which reads the token's k routed rows
+// through inv_perm, then its shared-expert rows, then the residual, and sums them in fp32
+// in exactly that order before a single rounding.  Loads and stores are 16 bytes per lane,
+// so the kernel streams rows at HBM rate.
 #include "moe_internal.h"
 
 namespace moe {

@@ -10,14 +10,15 @@
  *   moe_forward      the whole layer (optionally RMSNorm first, residual last)
  *
  * What is computed follows the pages this library is built from: a router sends each
- * token to k of E experts (dispatch README, intro; switchyard page, hero: "8 of the 64
- * experts"), rows are sorted by expert with a prefix scan and no atomics (switchyard
- * §02 "Route and sort"), each expert is a SwiGLU block run for all experts in one launch
- * (switchyard §02 "One launch for all experts"), and the combine is atomic-free and
- * gives one bit-exact answer (switchyard hero "Bit-identical", §02 "No atomics").
- * Shared experts follow the DeepSeek-MoE layout (dispatch README, "Stack"); int8
- * weight-only experts follow dispatch's per-channel format ("What has been measured",
- * phase 5a).
+ * token to k of E experts (dispatch README, intro; switchyard page, opening paragraph:
+ * OLMoE routes each token to 8 of its 64 experts); rows are sorted by expert with a prefix
+ * scan and no atomics (switchyard §02 "Route and sort"); each expert is a SwiGLU block and
+ * all experts run in one launch (switchyard §02 "One launch for all experts"); the combine
+ * is atomic-free and its result does not depend on where experts ran (switchyard page,
+ * hero statistics: expert-parallel output equal to one GPU bit for bit; §02 "Kernels and
+ * dispatch").  Shared experts follow the DeepSeek-MoE layout (dispatch README, "Stack");
+ * int8 weight-only experts follow dispatch's per-channel format (dispatch README, "What has
+ * been measured", phase 5a).
  *
  * Conventions (every function):
  *  - Array arguments are DEVICE pointers allocated and owned by the caller.  The library
@@ -140,7 +141,8 @@ int32_t moe_grouped_ffn(const moe_layer_desc_t* desc, int32_t T, const void* x,
                         const int32_t* perm, const void* plan, void* rows, void* ws,
                         size_t ws_bytes, void* stream);
 
-/* Step 5 -- deterministic combine (switchyard hero "Bit-identical", §02 "No atomics"):
+/* Step 5 -- deterministic combine (switchyard page, hero statistics and §02 "Kernels and
+ * dispatch": an atomic-free result that does not depend on where the experts ran):
  *   y[t] = sum_{j<k} topk_w[t,j] * rows[inv_perm[t*k+j]] + sum_{s<S} rows[T*k+s*T+t]
  *          + residual[t]
  * summed in fp32 in exactly that order, rounded once to act_dtype.

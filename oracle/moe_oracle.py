@@ -15,14 +15,15 @@ What the layer computes, from the pages:
 
 * routing -- each token is sent to ``k`` of ``E`` experts by top-k gating
   (dispatch README, intro and "Why this project"; switchyard page, hero:
-  "8 of the 64 experts", and §02 "Route and sort");
+  OLMoE routes each token to 8 of its 64 experts, and §02 "Route and sort");
 * the rows routed to an expert are grouped together, sorted by expert
   (switchyard §02 "Route and sort");
 * each expert is a SwiGLU feed-forward block (switchyard §02 "One launch for
   all experts"; "What switchyard adds", item 1);
 * the expert outputs are combined back per token, weighted by the gate, with a
   unique answer that does not depend on where the experts ran (switchyard hero,
-  "Bit-identical", and §02 "No atomics");
+  statistics: expert-parallel output equal to one GPU bit for bit, and §02
+  "Kernels and dispatch": no atomics);
 * DeepSeek-style layers add always-on shared experts to the routed ones
   (dispatch README, "Stack");
 * int8 weight-only experts are per-channel quantised and dequantised inside

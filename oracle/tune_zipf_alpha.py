@@ -1,7 +1,7 @@
 """Find the Zipf exponent of the 16-layer prefill stack (writes nothing; prints it).
 
-The stack's routing skew is stated as "the busiest expert receives about 4x the
-mean load" (the switchyard page, §03 "Load balance", measures 4.0x at 2,048
+The stack's routing is skewed so that its busiest expert gets about four times
+the mean load (the switchyard page, §03 "Load balance", measures 4.0x at 2,048
 tokens per GPU).  The skew comes from a router bias ``alpha * ln(1/rank)`` over
 a seeded ranking of the experts; this script bisects ``alpha`` on layer 0 of
 the stack, with the oracle's own RMSNorm, logits and top-k, until
