@@ -3,29 +3,49 @@
 // The switchyard page runs all experts' GEMMs in one launch with the SwiGLU fused into the
 // epilogue (§02 "One launch for all experts"); here that is one launch per matrix pair on
 // gfx950's v_mfma_f32_16x16x32_bf16.  Work items come from the launch plan written by the
-// permute kernel: blockIdx.y is an M-tile (group, first row) of the sorted rows, blockIdx.x
-// an N-tile; tiles past the plan's count exit at once, so the grid can be sized from T*k
+// permute kernel: each workgroup maps to one (M-tile, N-tile) of one group, in an XCD-aware
+// order; work past the plan's count exits at once, so the grid can be sized from T*k
 // without reading counts back to the host.
 //
-// Tile: BM=128 rows x 128 columns, BK=64, four wavefronts in a 2x2 layout, each owning a
-// 64x64 accumulator block (sixteen 16x16 MFMA tiles).  For gate/up the 128 columns are 64
-// gate channels followed by the same 64 up channels, and every wavefront holds matching
-// gate and up tiles, so silu(g)*u is formed in registers.  A rows are gathered through perm
-// (token rows of x) or read in order (h rows); both operands are staged K-contiguous in LDS
-// (row pitch padded by 16 bytes), double-buffered with a register prefetch of the next
-// K-step.  int8 weights are widened to bf16 (exact) as they are written to LDS; the
-// per-channel scale multiplies the fp32 accumulator in the epilogue.
+// Both kernels use 128-row M-tiles.  For gate/up an N-tile holds n gate channels followed by
+// the same n up channels, and every wavefront holds matching gate and up accumulators, so
+// silu(g)*u is formed in registers.  A rows are gathered through perm (token rows of x) or
+// read in order (h rows).  128 rows keep the padding of the last tile of each expert small
+// under skewed routing, where most experts get a few hundred rows.
+//
+//  * k_gemm_ring (bf16 weights, K a multiple of 32): 128x256 tiles, eight wavefronts in a
+//    2x4 layout each owning 64x64 (sixteen 16x16 MFMA tiles).  BK=32 and a ring of NST LDS stages
+//    filled directly from global memory by global_load_lds_dwordx4, issued NST-1 stages
+//    ahead of the MFMAs, so several stages of loads are always in flight without holding
+//    registers.  The DMA writes lane l's 16 bytes at base + 16*l, so a stage is row-major
+//    with 64-byte rows; the XOR swizzle that keeps the MFMA operand reads free of bank
+//    conflicts is applied on the source side (each lane fetches a permuted 16-byte chunk
+//    of its row).
+//  * k_gemm (any K, int8 weights): 128x128 tiles, four wavefronts in a 2x2 layout each
+//    owning 64x64.  BK=64, LDS double buffer (rows padded by 16 bytes) with
+//    a register prefetch of the next K-step; int8 weights are widened to bf16 (exact) on
+//    the way into LDS.  The per-channel int8 scale multiplies the fp32 accumulator in the
+//    epilogue.
 #include "moe_internal.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int PITCH = BK + 8;                  // bf16 elements per LDS row
+constexpr int BM = 128, BN = 128;
+constexpr int THREADS = 256;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
+
+// general kernel
+constexpr int BK = 64;
+constexpr int PITCH = BK + 8;  // bf16 elements per LDS row
 constexpr int A_ELEMS = BM * PITCH, B_ELEMS = BN * PITCH;
 constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
 constexpr size_t GEMM_LDS = 2 * STAGE_ELEMS * sizeof(uint16_t);
+
+// ring kernel
+constexpr int RBK = 32;  // K elements per stage
+constexpr int RNST = 3;  // stages in the ring (two workgroups per CU fit in LDS)
 
 struct GemmArgs {
   const void* in;   // gate/up: x [T, K] (gathered through perm); down: h [R, K]
@@ -38,7 +58,120 @@ struct GemmArgs {
   const int32_t* plan;
   void* out;        // [R, N]
   int K, N, k, E, max_groups;
+  int n_blk;        // output channels per N-tile (half the tile width for gate/up, all of it for down)
 };
+
+struct Work {
+  int g, r0, M, m0, n0;
+};
+
+// XCD-aware work order.  Workgroups are dispatched round-robin over the 8 XCDs, so workgroup
+// w runs on XCD w % 8.  XCD x takes a contiguous slice of the logical order (group, N-tile,
+// M-tile): the M-tiles sharing a weight tile, and the N-tiles sharing a group's activation
+// rows, run on the same L2 at about the same time.  The slice size comes from the plan's
+// tile count, so every XCD gets valid work.  Returns false for a workgroup with no work.
+template <int TBM>
+__device__ __forceinline__ bool map_work_t(const GemmArgs& a, Work& w) {
+  const int32_t* plan = a.plan;
+  const int NT = (a.N + a.n_blk - 1) / a.n_blk;  // N-tiles per group
+  const int valid = plan[1] * NT;
+  const int per_xcd = (valid + kXcds - 1) / kXcds;
+  const int wid = blockIdx.x;
+  const int L = (wid % kXcds) * per_xcd + wid / kXcds;
+  if (wid / kXcds >= per_xcd || L >= valid) return false;
+  const int32_t* tiles = plan + kPlanHeader + a.max_groups;
+  const int p = L / NT;  // a tile of the group that owns L
+  w.g = tiles[2 * p];
+  w.r0 = a.offsets[w.g];
+  w.M = a.offsets[w.g + 1] - w.r0;
+  const int mt = (w.M + TBM - 1) / TBM;           // the group's M-tiles
+  const int first = p - tiles[2 * p + 1] / TBM;   // the group's first tile in the list
+  const int o = L - first * NT;                   // position inside the group's (N, M) block
+  w.m0 = (o % mt) * TBM;
+  w.n0 = (o / mt) * a.n_blk;
+  return true;
+}
+
+// Row of the A operand for M-tile row m (clamped into the group; results discarded).
+// MODE 0 (gate/up) gathers token rows of x: through perm for a routed expert, row m itself
+// for a shared expert (which sees every token in order).  MODE 1 (down) reads h row r0 + m.
+template <int MODE>
+__device__ __forceinline__ const uint16_t* a_row_t(const GemmArgs& a, const Work& w, int m) {
+  m = min(m, w.M - 1);
+  const int r = w.r0 + m;
+  size_t src;
+  if (MODE == 0)
+    src = (w.g < a.E) ? (size_t)(a.perm[r] / a.k) : (size_t)m;
+  else
+    src = (size_t)r;
+  return reinterpret_cast<const uint16_t*>(a.in) + src * a.K;
+}
+
+// Weight row (output channel) for B-tile row `row` (clamped into the matrix).
+template <int MODE, int TBN>
+__device__ __forceinline__ const unsigned char* b_row_t(const GemmArgs& a, const Work& w, int row,
+                                                        int esz) {
+  int n;
+  const void* base;
+  if (MODE == 0) {
+    n = w.n0 + (row % (TBN / 2));
+    base = row < TBN / 2 ? a.w0 : a.w1;
+  } else {
+    n = w.n0 + row;
+    base = a.w0;
+  }
+  n = min(n, a.N - 1);
+  return reinterpret_cast<const unsigned char*>(base) + ((size_t)w.g * a.N + n) * a.K * esz;
+}
+
+// The four B-tile rows a lane feeds to its wavefront's MFMAs (j = 0..3).
+template <int MODE>
+__device__ __forceinline__ int b_frag_row(int wn, int j, int lr) {
+  if (MODE == 0)  // j = 0,1: gate channels; j = 2,3: the same up channels
+    return (j < 2 ? 0 : BN / 2) + wn * 32 + (j % 2) * 16 + lr;
+  return wn * 64 + j * 16 + lr;
+}
+
+// Epilogue: lane holds rows 4*(lane/16) + v, column lane%16 of each 16x16 tile.
+template <int MODE, bool I8>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const Work& w, int wm, int wn,
+                                           int lane, const f32x4 (&acc)[4][4]) {
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const int N = a.N, lr = lane % 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = w.m0 + wm * 64 + i * 16 + (lane / 16) * 4 + v;
+      if (m >= w.M) continue;
+      const size_t orow = (size_t)(w.r0 + m) * N;
+      if (MODE == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = w.n0 + wn * 32 + j * 16 + lr;
+          if (n < N) {
+            float gv = acc[i][j][v], uv = acc[i][j + 2][v];
+            if (I8) {
+              gv *= a.s0[(size_t)w.g * N + n];
+              uv *= a.s1[(size_t)w.g * N + n];
+            }
+            out[orow + n] = f32_to_bf16(silu(gv) * uv);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = w.n0 + wn * 64 + j * 16 + lr;
+          if (n < N) {
+            float ov = acc[i][j][v];
+            if (I8) ov *= a.s0[(size_t)w.g * N + n];
+            out[orow + n] = f32_to_bf16(ov);
+          }
+        }
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
@@ -55,67 +188,40 @@ __device__ __forceinline__ void i8x16_to_bf16x16(const uint4& q, uint4& lo, uint
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// MODE 0: h = silu(x W_gate^T) * (x W_up^T); MODE 1: rows = h W_down^T
+// ------------------------------------------------------------------------------------------
+// general kernel: MODE 0: h = silu(x W_gate^T) * (x W_up^T); MODE 1: rows = h W_down^T
+// ------------------------------------------------------------------------------------------
 template <int MODE, bool I8>
-__global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
+__global__ __launch_bounds__(THREADS) void k_gemm(const GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  const int tile = blockIdx.y;
-  const int32_t* plan = a.plan;
-  if (tile >= plan[1]) return;
-  const int32_t* tiles = plan + kPlanHeader + a.max_groups;
-  const int g = tiles[2 * tile], m0 = tiles[2 * tile + 1];
-  const int r0 = a.offsets[g];
-  const int M = a.offsets[g + 1] - r0;
-  const int K = a.K, N = a.N;
+  Work w;
+  if (!map_work_t<BM>(a, w)) return;
+  const int K = a.K;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
-  // ---- global -> register staging assignments
-  // A: 128 rows x 8 chunks of 16 B; thread owns rows (tid/8) + 32*i, chunk tid%8
+  // A: 128 rows x 8 chunks of 16 B per K-step; thread owns rows tid/8 + 32*i, chunk tid%8
+  constexpr int A_LOADS = BM * 8 / THREADS;
   const int a_chunk = tid % 8;
-  const uint16_t* a_src[4];
+  const uint16_t* a_src[A_LOADS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = min(m0 + tid / 8 + 32 * i, M - 1);
-    const int r = r0 + m;
-    size_t src_row;
-    if (MODE == 0)
-      src_row = (g < a.E) ? (size_t)(a.perm[r] / a.k) : (size_t)m;
-    else
-      src_row = (size_t)r;
-    a_src[i] = reinterpret_cast<const uint16_t*>(a.in) + src_row * K;
-  }
-  // B: 128 rows; bf16: 8 chunks of 16 B per row, rows (tid/8) + 32*i
-  //              int8: 4 chunks of 16 B per row, rows (tid/4) + 64*i
-  constexpr int B_LOADS = I8 ? 2 : 4;
-  constexpr int B_CPR = I8 ? 4 : 8;   // 16-byte chunks per row per K-step
+  for (int i = 0; i < A_LOADS; ++i) a_src[i] = a_row_t<MODE>(a, w, w.m0 + tid / 8 + (THREADS / 8) * i);
+  // B: 128 rows; bf16: 8 chunks of 16 B per row, int8: 4 chunks of 16 B per row
+  constexpr int B_CPR = I8 ? 4 : 8;
+  constexpr int B_LOADS = BN * B_CPR / THREADS;
   const int b_chunk = tid % B_CPR;
   const unsigned char* b_src[B_LOADS];
-  int b_row[B_LOADS];
-  const int n_blk = MODE == 0 ? BN / 2 : BN;
-  const int n0 = blockIdx.x * n_blk;
+  int b_rowi[B_LOADS];
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
-    const int row = tid / B_CPR + (256 / B_CPR) * i;
-    b_row[i] = row;
-    int n;
-    const void* base;
-    if (MODE == 0) {
-      n = n0 + (row % (BN / 2));
-      base = row < BN / 2 ? a.w0 : a.w1;
-    } else {
-      n = n0 + row;
-      base = a.w0;
-    }
-    n = min(n, N - 1);
-    const size_t esz = I8 ? 1 : 2;
-    b_src[i] = reinterpret_cast<const unsigned char*>(base) + ((size_t)g * N + n) * K * esz;
+    b_rowi[i] = tid / B_CPR + (THREADS / B_CPR) * i;
+    b_src[i] = b_row_t<MODE, BN>(a, w, b_rowi[i], I8 ? 1 : 2);
   }
 
-  uint4 ra[4], rb[B_LOADS];
+  uint4 ra[A_LOADS], rb[B_LOADS];
   auto load_stage = [&](int kt) {
     const int kb = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < A_LOADS; ++i) {
       const int col = kb + a_chunk * 8;
       ra[i] = col < K ? *reinterpret_cast<const uint4*>(a_src[i] + col) : zero4();
     }
@@ -130,11 +236,11 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     uint16_t* As = lds + buf * STAGE_ELEMS;
     uint16_t* Bs = As + A_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(As + (tid / 8 + 32 * i) * PITCH + a_chunk * 8) = ra[i];
+    for (int i = 0; i < A_LOADS; ++i)
+      *reinterpret_cast<uint4*>(As + (tid / 8 + (THREADS / 8) * i) * PITCH + a_chunk * 8) = ra[i];
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      uint16_t* dst = Bs + b_row[i] * PITCH;
+      uint16_t* dst = Bs + b_rowi[i] * PITCH;
       if (I8) {
         uint4 lo, hi;
         i8x16_to_bf16x16(rb[i], lo, hi);
@@ -146,17 +252,11 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     }
   };
 
-  // ---- MFMA layout: wave (wm, wn) owns rows wm*64.., 4x4 tiles of 16x16
   const int wm = wave / 2, wn = wave % 2;
   const int lr = lane % 16, lk = (lane / 16) * 8;
   int brow[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (MODE == 0)  // j = 0,1: gate channels; j = 2,3: the same up channels
-      brow[j] = (j < 2 ? 0 : BN / 2) + wn * 32 + (j % 2) * 16 + lr;
-    else
-      brow[j] = wn * 64 + j * 16 + lr;
-  }
+  for (int j = 0; j < 4; ++j) brow[j] = b_frag_row<MODE>(wn, j, lr);
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -189,68 +289,202 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     if (kt + 1 < nk) store_stage((kt + 1) & 1);
     __syncthreads();
   }
+  store_tile<MODE, I8>(a, w, wm, wn, lane, acc);
+}
 
-  // ---- epilogue: lane holds rows 4*(lane/16) + v, column lane%16 of each 16x16 tile
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+// ------------------------------------------------------------------------------------------
+// ring kernel (bf16 weights, K % 32 == 0)
+// ------------------------------------------------------------------------------------------
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
+
+// Tile RBM x RBN (gate/up: RBN/2 gate + the same RBN/2 up channels), WM x WN wavefronts,
+// each owning (RBM/WM) x (RBN/WN); K advances RBK=32 per stage through an RNST-deep ring.
+constexpr int RBM = 128, RBN = 256, RWM = 2, RWN = 4;
+constexpr int R_THREADS = 64 * RWM * RWN;
+constexpr int R_TI = RBM / RWM / 16, R_TJ = RBN / RWN / 16;  // 16x16 MFMA tiles per wavefront
+constexpr int R_A_BYTES = RBM * RBK * 2, R_STAGE = (RBM + RBN) * RBK * 2;
+constexpr int R_DMA_A = RBM / 16 / (RWM * RWN), R_DMA_B = RBN / 16 / (RWM * RWN);  // per wave
+constexpr int R_LPS = R_DMA_A + R_DMA_B;  // loads per stage per wavefront
+constexpr size_t R_LDS = (size_t)RNST * R_STAGE;
+static_assert((RNST - 2) * R_LPS < 16, "vmcnt range");
+
+template <int MODE>
+__global__ __launch_bounds__(R_THREADS) void k_gemm_ring(const GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char rlds[];
+  Work w;
+  if (!map_work_t<RBM>(a, w)) return;
+  const int K = a.K;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+  // DMA assignment: a stage holds RBM A-rows then RBN B-rows of 64 B each; one 1 KiB load
+  // covers 16 rows.  Wavefront `wave` issues A loads q = wave*R_DMA_A + i and B loads
+  // q = wave*R_DMA_B + i.  Lane l of a load fills row 16q + l/4, position l%4, with the
+  // row's 16-byte chunk (l%4) ^ swz(row), swz(row) = (row >> 2) & 3.
+  const uint16_t* a_src[R_DMA_A];
+  const uint16_t* b_src[R_DMA_B];
+  int ca[R_DMA_A], cb[R_DMA_B];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < R_DMA_A; ++i) {
+    const int row = 16 * (wave * R_DMA_A + i) + lane / 4;
+    ca[i] = ((lane % 4) ^ ((row >> 2) & 3)) * 8;
+    a_src[i] = a_row_t<MODE>(a, w, w.m0 + row);
+  }
+#pragma unroll
+  for (int i = 0; i < R_DMA_B; ++i) {
+    const int row = 16 * (wave * R_DMA_B + i) + lane / 4;
+    cb[i] = ((lane % 4) ^ ((row >> 2) & 3)) * 8;
+    b_src[i] = reinterpret_cast<const uint16_t*>(b_row_t<MODE, RBN>(a, w, row, 2));
+  }
+  auto issue = [&](int kt) {
+    unsigned char* st = rlds + (kt % RNST) * R_STAGE;
+    const int kb = kt * RBK;
+#pragma unroll
+    for (int i = 0; i < R_DMA_A; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(a_src[i] + kb + ca[i]),
+                                       (lds_void*)(st + (wave * R_DMA_A + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < R_DMA_B; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(b_src[i] + kb + cb[i]),
+                                       (lds_void*)(st + R_A_BYTES + (wave * R_DMA_B + i) * 1024), 16,
+                                       0, 0);
+  };
+
+  const int wm = wave / RWN, wn = wave % RWN;
+  const int lr = lane % 16;
+  // operand reads: row r (a multiple of 16 plus lr), logical chunk c = lane/16 -> byte
+  // offset r*64 + ((c ^ swz(r)) * 16); swz(r) = (lr >> 2) & 3 since r - lr is a multiple of 16
+  const int rd_chunk = ((lane / 16) ^ ((lr >> 2) & 3)) * 16;
+  int a_off[R_TI], b_off[R_TJ];
+#pragma unroll
+  for (int i = 0; i < R_TI; ++i) a_off[i] = (wm * (RBM / RWM) + i * 16 + lr) * 64 + rd_chunk;
+#pragma unroll
+  for (int j = 0; j < R_TJ; ++j) {
+    int row;
+    if (MODE == 0)  // first half of the tiles: gate channels, second half: the same up channels
+      row = (j < R_TJ / 2 ? 0 : RBN / 2) + wn * (RBN / RWN / 2) + (j % (R_TJ / 2)) * 16 + lr;
+    else
+      row = wn * (RBN / RWN) + j * 16 + lr;
+    b_off[j] = R_A_BYTES + row * 64 + rd_chunk;
+  }
+
+  f32x4 acc[R_TI][R_TJ];
+#pragma unroll
+  for (int i = 0; i < R_TI; ++i)
+#pragma unroll
+    for (int j = 0; j < R_TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / RBK;
+#pragma unroll
+  for (int s = 0; s < RNST - 1; ++s)
+    if (s < nk) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt is complete once at most (stages issued after it) * R_LPS loads are pending
+    const int ahead = min(nk - 1, kt + RNST - 2) - kt;
+    if (ahead >= 2)
+      wait_vmcnt<2 * R_LPS>();
+    else if (ahead == 1)
+      wait_vmcnt<R_LPS>();
+    else
+      wait_vmcnt<0>();
+    // Every wavefront waited for its own loads of stage kt above, so after this barrier the
+    // whole stage is in LDS and every wavefront is done with stage kt-1.  A plain s_barrier:
+    // __syncthreads() would add a release fence, i.e. wait for all loads in flight.
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + RNST - 1 < nk) issue(kt + RNST - 1);
+    const unsigned char* st = rlds + (kt % RNST) * R_STAGE;
+    bf16x8 bfr[R_TJ];
+#pragma unroll
+    for (int j = 0; j < R_TJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
+#pragma unroll
+    for (int i = 0; i < R_TI; ++i) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
+#pragma unroll
+      for (int j = 0; j < R_TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: lane holds rows 4*(lane/16) + v, column lane%16 of each 16x16 tile
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const int N = a.N;
+#pragma unroll
+  for (int i = 0; i < R_TI; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int m = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + v;
-      if (m >= M) continue;
-      const size_t orow = (size_t)(r0 + m) * N;
+      const int m = w.m0 + wm * (RBM / RWM) + i * 16 + (lane / 16) * 4 + v;
+      if (m >= w.M) continue;
+      const size_t orow = (size_t)(w.r0 + m) * N;
       if (MODE == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 32 + j * 16 + lr;
-          if (n < N) {
-            float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-            if (I8) {
-              gv *= a.s0[(size_t)g * N + n];
-              uv *= a.s1[(size_t)g * N + n];
-            }
-            out[orow + n] = f32_to_bf16(silu(gv) * uv);
-          }
+        for (int j = 0; j < R_TJ / 2; ++j) {
+          const int n = w.n0 + wn * (RBN / RWN / 2) + j * 16 + lr;
+          if (n < N) out[orow + n] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + R_TJ / 2][v]);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 64 + j * 16 + lr;
-          if (n < N) {
-            float ov = acc[i][j][v];
-            if (I8) ov *= a.s0[(size_t)g * N + n];
-            out[orow + n] = f32_to_bf16(ov);
-          }
+        for (int j = 0; j < R_TJ; ++j) {
+          const int n = w.n0 + wn * (RBN / RWN) + j * 16 + lr;
+          if (n < N) out[orow + n] = f32_to_bf16(acc[i][j][v]);
         }
       }
     }
   }
 }
 
+template <typename F>
+hipError_t set_lds(F* kernel, size_t bytes, bool& done) {
+  if (done) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+// The ring kernel serves bf16 weights when both K dimensions are multiples of its K-step;
+// both launches of a layer must use the same M-tile (it is baked into the launch plan).
+bool use_ring(const LayerDims& L) { return L.wdt == MOE_BF16 && L.d % RBK == 0 && L.I % RBK == 0; }
+
 template <int MODE, bool I8>
-hipError_t run_gemm(const GemmArgs& a, int max_tiles, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE, I8>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+hipError_t run_gemm(GemmArgs a, int max_tiles, bool ring, hipStream_t s) {
+  const int tbn = ring ? RBN : BN;
+  a.n_blk = MODE == 0 ? tbn / 2 : tbn;
+  const int nt = (a.N + a.n_blk - 1) / a.n_blk;
+  // one workgroup per possible (M-tile, N-tile), rounded up to a multiple of the XCD count
+  int grid = max_tiles * nt;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  hipError_t e;
+  if (ring && !I8) {
+    static bool done = false;
+    if ((e = set_lds(&k_gemm_ring<MODE>, R_LDS, done)) != hipSuccess) return e;
+    LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
+    k_gemm_ring<MODE><<<grid, R_THREADS, R_LDS, s>>>(a);
+  } else {
+    static bool done = false;
+    if ((e = set_lds(&k_gemm<MODE, I8>, GEMM_LDS, done)) != hipSuccess) return e;
+    LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
+    k_gemm<MODE, I8><<<grid, THREADS, GEMM_LDS, s>>>(a);
   }
-  const int n_blk = MODE == 0 ? BN / 2 : BN;
-  dim3 grid((a.N + n_blk - 1) / n_blk, max_tiles);
-  LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-  k_gemm<MODE, I8><<<grid, 256, GEMM_LDS, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_tile_m() { return BM; }
+int gemm_tile_m(const LayerDims& L) { return use_ring(L) ? RBM : BM; }
 
 hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
+  const bool ring = use_ring(L);
+  const int tm = ring ? RBM : BM;
   const int max_tiles = (int)plan_max_tiles(T, L.k, L.E, L.S);
-  // tiles of height BM can never exceed this bound (it is computed for height 16)
-  const int tiles = (T * L.k) / BM + (T * L.k < L.E ? T * L.k : L.E) + L.S * ((T + BM - 1) / BM) + 1;
+  // tiles of height tm can never exceed this bound (the plan is sized for height 16)
+  const int tiles = (T * L.k) / tm + (T * L.k < L.E ? T * L.k : L.E) + L.S * ((T + tm - 1) / tm) + 1;
   const int grid_tiles = tiles < max_tiles ? tiles : max_tiles;
   GemmArgs a{};
   a.offsets = f.offsets;
@@ -270,7 +504,7 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.h;
   a.K = L.d;
   a.N = L.I;
-  err = i8 ? run_gemm<0, true>(a, grid_tiles, s) : run_gemm<0, false>(a, grid_tiles, s);
+  err = i8 ? run_gemm<0, true>(a, grid_tiles, false, s) : run_gemm<0, false>(a, grid_tiles, ring, s);
   if (err != hipSuccess) return err;
 
   a.in = f.h;
@@ -281,7 +515,7 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.rows;
   a.K = L.I;
   a.N = L.d;
-  return i8 ? run_gemm<1, true>(a, grid_tiles, s) : run_gemm<1, false>(a, grid_tiles, s);
+  return i8 ? run_gemm<1, true>(a, grid_tiles, false, s) : run_gemm<1, false>(a, grid_tiles, ring, s);
 }
 
 }  // namespace moe

@@ -143,7 +143,7 @@ LaunchTimer::~LaunchTimer() {
 
 int ffn_tile_m(const LayerDims& L, int T) {
   if (L.act == MOE_F32) return 0;
-  return T > 32 ? gemm_tile_m() : 0;
+  return T > 32 ? gemm_tile_m(L) : 0;
 }
 
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s) {

@@ -188,7 +188,7 @@ int ffn_tile_m(const LayerDims& L, int T);
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
 hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
 hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
-int gemm_tile_m();
+int gemm_tile_m(const LayerDims& L);
 
 hipError_t launch_combine(const LayerDims& L, int T, const void* rows, const int32_t* inv_perm,
                           const float* topk_w, const void* residual, void* y, hipStream_t s);

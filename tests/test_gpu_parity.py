@@ -157,10 +157,15 @@ SMALL_RAGGED = S.Workload("small_ragged", 90, d=272, E=8, k=2, I=208, S=1, renor
 SMALL_RAGGED_I8 = dataclasses.replace(SMALL_RAGGED, name="small_ragged_i8", cid=91, wdt="i8")
 SMALL_ZIPF = dataclasses.replace(SMALL_RAGGED, name="small_zipf", cid=92, routing="zipf",
                                  zipf_alpha=2.0, router_std=0.05, tokens=(300,))
+# bf16 layer on the LDS-ring MFMA path (d and I multiples of 32) whose N-tiles are ragged in
+# both GEMMs (I=352 is not a multiple of 128 channels, d=288 not of 256)
+SMALL_RING = S.Workload("small_ring", 93, d=288, E=8, k=2, I=352, S=1, renormalize=True,
+                        tokens=(300,))
 
 FULL_CASES = [  # every row checked
     (S.TINY_F32, 16), (SMALL_RAGGED, 100), (SMALL_RAGGED, 7), (SMALL_RAGGED_I8, 100),
-    (SMALL_RAGGED_I8, 5), (SMALL_ZIPF, 300), (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8),
+    (SMALL_RAGGED_I8, 5), (SMALL_ZIPF, 300), (SMALL_RING, 300), (SMALL_RING, 40),
+    (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8),
     (S.OLMOE_I8, 1), (S.OLMOE_I8, 8), (S.DEEPSEEK_BF16, 1), (S.OLMOE_I8_ZIPF, 8),
 ]
 SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
