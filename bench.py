@@ -11,8 +11,16 @@ against the fp64 CPU oracle; a disagreeing build is refused, not timed.
 
 The expert weights are replicated ``--copies`` times and the steps rotate over
 the copies, so the 256 MiB Infinity Cache cannot serve the weights of the next
-step.  The dominant kernel (grouped gate/up) is additionally timed per launch
-with HIP events through the library's one-shot timing hook, for the roofline.
+step (``copies_plateau`` shows the time no longer falls with more copies).  The
+dominant kernel (grouped gate/up) is additionally timed per launch with HIP
+events through the library's one-shot timing hook, for the roofline.  The same
+steps are also captured once in a HIP graph and replayed (checked bit for bit
+against the eager result first).
+
+After the headline, the other workload points are timed (``--sweep``), then the
+16-layer prefill stack (RMSNorm + MoE + residual per layer, T=2048, Zipf
+routing with the busiest expert at about 4x the mean), then the oracle on the
+host cores as a reported CPU baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload olmoe_bf16 --tokens 8]
 Prints ONE JSON line.
@@ -20,7 +28,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
-import dataclasses
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +40,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+DEFAULT_SWEEP = ("olmoe_bf16:1,olmoe_bf16:64,olmoe_i8:1,olmoe_i8:8,olmoe_i8:64,olmoe_i8_zipf:8,"
+                 "deepseek_bf16:1,deepseek_bf16:16,deepseek_bf16:128,deepseek_bf16:512,"
+                 "deepseek_bf16:2048")
 
 
 def parse():
@@ -42,12 +55,18 @@ def parse():
     p.add_argument("--workload", default="olmoe_bf16")
     p.add_argument("--tokens", type=int, default=8)
     p.add_argument("--copies", type=int, default=8, help="weight replicas rotated over (cache defeat)")
-    p.add_argument("--sweep", default="olmoe_bf16:1,olmoe_bf16:64,olmoe_i8:1,olmoe_i8:8,"
-                   "deepseek_bf16:1,deepseek_bf16:16,deepseek_bf16:2048",
+    p.add_argument("--sweep", default=DEFAULT_SWEEP,
                    help="extra workload:T points timed after the headline ('' for none)")
     p.add_argument("--sweep-steps", type=int, default=20)
+    p.add_argument("--no-stack", action="store_true", help="skip the 16-layer prefill stack")
+    p.add_argument("--stack-steps", type=int, default=5, help="timed passes over the 16 layers")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip graph replay, copies plateau and copy ceiling")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--counters-pass", action="store_true",
+                   help="for rocprofv3 --pmc runs: a 256 MiB device copy (the counters' "
+                        "calibration), then the headline steps only; prints no JSON")
     return p.parse_args()
 
 
@@ -78,6 +97,154 @@ def layer_work(wl, T, n_touched_routed):
     }
 
 
+def mfma_bound(wl, T):
+    """The prefill regime: bf16 layers at T >= 512 are priced against the matrix peak."""
+    return T >= 512 and wl.act == "bf16"
+
+
+# ------------------------------------------------------------------------------------------
+# timing helpers (all on torch's current stream, which is the stream the library launches on)
+# ------------------------------------------------------------------------------------------
+def _events(n):
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:  # torch creates the HIP events on first record
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def time_steps(step, steps, warmup):
+    """Mean ms of one step over exactly `steps` steps bracketed by synchronisations."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def step_percentiles(step, n):
+    """p10 / median / p90 of single steps, each bracketed by its own event pair."""
+    import numpy as np
+    import torch
+    evs = _events(n)
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"p10": round(float(np.percentile(d, 10)), 5), "p50": round(float(np.median(d)), 5),
+            "p90": round(float(np.percentile(d, 90)), 5)}
+
+
+def time_kernel(kernel, launch, launches):
+    """Average duration (ms) of one kernel, bracketed by HIP events that the library records
+    on the kernel's own stream around its next launch; `launch(i)` runs one layer."""
+    import torch
+
+    from grouped_expert_ffn_amd import abi
+    evs = _events(launches)
+    for i, (a, b) in enumerate(evs):
+        abi.moe_time_next_launch(kernel, a, b)
+        launch(i)
+    torch.cuda.synchronize()
+    ds = [a.elapsed_time(b) for a, b in evs]
+    return sum(ds) / len(ds), min(ds)
+
+
+def graph_replay(capture_calls, y, reference, replays):
+    """Capture `capture_calls(stream)` once in a HIP graph, check that replays reproduce
+    `reference` bit for bit (with eager work and synchronisations in between), then time
+    `replays` replays.  Returns ms per replay."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        capture_calls(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, reference):
+            raise SystemExit("graph replay differs from the eager result; refusing to time it")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / replays
+    del g
+    return ms
+
+
+def copy_ceiling_gbs(mib=1024, reps=10):
+    """Read + write bandwidth of a plain device-to-device copy (context for the peak)."""
+    import torch
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * (mib << 20) / (ms * 1e-3) / 1e9, 1)
+
+
+# ------------------------------------------------------------------------------------------
+# HBM traffic from a committed rocprofv3 PMC summary, valid only for the kernel source it
+# was taken on
+# ------------------------------------------------------------------------------------------
+def _sources_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(summary_name):
+    """Bytes per launch = FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale (KiB), from
+    `profiles/<summary_name>`; None when the summary is missing or its kernel sources have
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, summary_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        srcs = [s.strip() for s in kv["sources"].split(",")]
+        if _sources_digest(srcs) != kv["sources_sha256"]:
+            return None
+        kib = (float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+               + float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]))
+    except (KeyError, ValueError, OSError):
+        return None
+    return int(kib * 1024)
+
+
 # ------------------------------------------------------------------------------------------
 # one workload point on the GPU
 # ------------------------------------------------------------------------------------------
@@ -93,12 +260,29 @@ def host_layer(wl, seed=0):
     return _HOST[key]
 
 
+def _forward_args(desc, T, x, L, residual, y, ws, stream):
+    import ctypes
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    return (ctypes.byref(desc), T, x.data_ptr(), L.w_router.data_ptr(), ptr(L.bias),
+            ctypes.byref(L.weights), ptr(residual), y.data_ptr(), None, None, ws.data_ptr(),
+            ws.numel(), stream)
+
+
+def _call(lib, args):
+    st = lib.moe_forward(*args)
+    if st != 0:
+        from grouped_expert_ffn_amd import abi
+        raise abi.MoeError(st, "moe_forward", abi.last_error())
+
+
 class Point:
+    """One layer at T tokens, its weights replicated `copies` times on the GPU."""
+
     def __init__(self, wl, T, copies, seed=0):
         import torch
 
         import moe_synth as S
-        from grouped_expert_ffn_amd import DTYPES, DeviceLayer, make_desc, to_device
+        from grouped_expert_ffn_amd import DTYPES, DeviceLayer, abi, make_desc, to_device
         self.wl, self.T = wl, T
         self.host = host_layer(wl, seed)
         self.x_host = S.make_tokens(wl, T, seed)
@@ -108,34 +292,24 @@ class Point:
         base = DeviceLayer(self.desc, h.w_router, h.bias, h.w_gate, h.w_up, h.w_down, h.s_gate,
                            h.s_up, h.s_down)
         self.layers = [base]
+        c = lambda t: None if t is None else t.clone()  # noqa: E731
         for _ in range(copies - 1):
-            c = lambda t: None if t is None else t.clone()  # noqa: E731
             self.layers.append(DeviceLayer(self.desc, base.w_router, base.bias, c(base.w_gate),
                                            c(base.w_up), c(base.w_down), c(base.s_gate),
                                            c(base.s_up), c(base.s_down)))
         self.x = to_device(self.x_host)
         self.y = torch.empty_like(self.x)
         self.ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
-        ws = base.workspace(T)
-        self.ws = ws
+        self.ws = base.workspace(T)
         # pre-marshalled ctypes arguments: the timed loop is one C call per step
-        import ctypes
-
-        from grouped_expert_ffn_amd import abi
         self.lib = abi.lib()
-        self.stream = torch.cuda.current_stream().cuda_stream
-        self.args = []
-        for L in self.layers:
-            self.args.append((ctypes.byref(self.desc), T, self.x.data_ptr(), L.w_router.data_ptr(),
-                              None if L.bias is None else L.bias.data_ptr(), ctypes.byref(L.weights),
-                              None, self.y.data_ptr(), None, None, ws.data_ptr(), ws.numel(),
-                              self.stream))
+        self.args = [self.args_for(L, torch.cuda.current_stream().cuda_stream) for L in self.layers]
+
+    def args_for(self, L, stream):
+        return _forward_args(self.desc, self.T, self.x, L, None, self.y, self.ws, stream)
 
     def step(self, i):
-        st = self.lib.moe_forward(*self.args[i % len(self.args)])
-        if st != 0:
-            from grouped_expert_ffn_amd import abi
-            raise abi.MoeError(st, "moe_forward", abi.last_error())
+        _call(self.lib, self.args[i % len(self.args)])
 
     def routing(self):
         import torch
@@ -157,47 +331,20 @@ class Point:
         w = O.gate_weights_for(logits, ids[tok], self.wl.renormalize)
         ref = O.moe_layer(self.x_host[tok], O.Experts.from_layer(self.host), ids[tok], w,
                           self.wl.S, self.wl.E)
-        got = y[tok]
-        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-        mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
-        lim = 1e-5 if self.wl.act == "f32" else 1e-2
-        if not (rel <= lim and mx <= 2e-2):
-            raise SystemExit(f"parity gate FAILED for {self.wl.name} T={T}: rel-L2 {rel:.3e}, "
-                             f"max-abs/max {mx:.3e}; refusing to time")
-        return rel
+        return _gate(self.wl, f"T={T}", y[tok], ref)
 
-    def time_steps(self, steps, warmup):
+    def graph_ms(self, replays):
+        """One graph holds one forward per weight copy; ms per layer of a replay."""
         import torch
-        for i in range(warmup):
+        for i in range(len(self.args)):
             self.step(i)
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record()
-        for i in range(steps):
-            self.step(i)
-        ev1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return ev0.elapsed_time(ev1) / steps, wall
+        ref = self.y.clone()
 
-    def time_kernel(self, kernel, launches):
-        """Average duration (ms) of one kernel, bracketed by HIP events on its stream."""
-        import torch
-
-        from grouped_expert_ffn_amd import abi
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(launches)]
-        for a, b in evs:  # torch creates the HIP events on first record
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        for i, (a, b) in enumerate(evs):
-            abi.moe_time_next_launch(kernel, a, b)
-            self.step(i)
-        torch.cuda.synchronize()
-        ds = [a.elapsed_time(b) for a, b in evs]
-        return sum(ds) / len(ds), min(ds)
+        def capture(stream):
+            for L in self.layers:
+                _call(self.lib, self.args_for(L, stream))
+        return graph_replay(capture, self.y, ref, replays) / len(self.layers)
 
     def free(self):
         import torch
@@ -206,20 +353,36 @@ class Point:
         torch.cuda.empty_cache()
 
 
-def roofline_for(pt, work, kern_ms):
-    if pt.T >= 512 and pt.wl.act == "bf16":
+def _gate(wl, what, got, ref):
+    import numpy as np
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    lim = 1e-5 if wl.act == "f32" else 1e-2
+    if not (rel <= lim and mx <= 2e-2):
+        raise SystemExit(f"parity gate FAILED for {wl.name} {what}: rel-L2 {rel:.3e}, "
+                         f"max-abs/max {mx:.3e}; refusing to time")
+    return rel
+
+
+def roofline_for(wl, T, work, kern_ms, traffic=None):
+    if mfma_bound(wl, T):
         achieved = work["gate_up_flops"] / (kern_ms * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": "grouped gate/up + SwiGLU (MFMA)", "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                "traffic": None, "flops_per_launch": work["gate_up_flops"],
+                "traffic": traffic, "flops_per_launch": work["gate_up_flops"],
                 "avg_launch_ms": round(kern_ms, 5)}
     achieved = work["gate_up_bytes"] / (kern_ms * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": "grouped gate/up + SwiGLU (GEMV)", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "bytes_per_launch": work["gate_up_bytes"], "avg_launch_ms": round(kern_ms, 5)}
+            "traffic": traffic, "bytes_per_launch": work["gate_up_bytes"], "avg_launch_ms": round(kern_ms, 5)}
 
 
-def measure(wl, T, steps, warmup, copies):
+def _fracs(work, ms):
+    return (round(work["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            round(work["layer_flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4))
+
+
+def measure(wl, T, steps, warmup, copies, extras=False):
     import numpy as np
 
     from grouped_expert_ffn_amd import abi
@@ -228,29 +391,141 @@ def measure(wl, T, steps, warmup, copies):
     ids = pt.routing()
     n_touched = int(np.count_nonzero(np.bincount(ids.ravel(), minlength=wl.E)))
     work = layer_work(wl, T, n_touched)
-    ms, wall = pt.time_steps(steps, warmup)
+    ms, wall = time_steps(pt.step, steps, warmup)
     launches = max(10, min(steps, 50))
-    gu_ms, gu_min = pt.time_kernel(abi.MOE_KERNEL_GATE_UP, launches)
-    dn_ms, _ = pt.time_kernel(abi.MOE_KERNEL_DOWN, launches)
+    gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, pt.step, launches)
+    dn_ms, _ = time_kernel(abi.MOE_KERNEL_DOWN, pt.step, launches)
+    hbm, mfma = _fracs(work, ms)
     res = {
         "workload": wl.name, "tokens": T, "ms_per_layer": round(ms, 5),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "layer_hbm_frac": round(work["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "layer_mfma_frac": round(work["layer_flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "layer_hbm_frac": hbm, "layer_mfma_frac": mfma,
         "gate_up_ms": round(gu_ms, 5), "down_ms": round(dn_ms, 5),
         "gate_up_hbm_frac": round(work["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "down_hbm_frac": round(work["down_bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "touched_experts": n_touched, "parity_rel_l2": float(f"{rel:.3e}"),
     }
-    roof = roofline_for(pt, work, gu_ms)
+    if mfma_bound(wl, T):
+        res["gate_up_mfma_frac"] = round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+        res["down_mfma_frac"] = round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+    if extras:
+        res["step_ms_percentiles"] = step_percentiles(pt.step, steps)
+        res["graph_ms_per_layer"] = round(pt.graph_ms(max(4, steps // copies)), 5)
+    roof = roofline_for(wl, T, work, gu_ms)
     pt.free()
     return res, roof, ms, wall, work
 
 
+def copies_plateau(wl, T, counts=(1, 2, 4, 8, 16), steps=32):
+    """Layer time against the number of weight copies rotated over: it falls while the
+    Infinity Cache still holds the next step's weights, then stays flat."""
+    out = {}
+    for n in counts:
+        pt = Point(wl, T, n)
+        ms, _ = time_steps(pt.step, steps, 4)
+        out[str(n)] = round(ms, 5)
+        pt.free()
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# the 16-layer prefill stack: h <- h + MoE_l(RMSNorm(h)), l = 0..15, every pass from the same
+# input (layers ping-pong between two buffers, so no copy is timed)
+# ------------------------------------------------------------------------------------------
+class Stack:
+    def __init__(self, wl, T):
+        import torch
+
+        import moe_synth as S
+        from grouped_expert_ffn_amd import DTYPES, DeviceLayer, abi, make_desc, to_device
+        self.wl, self.T = wl, T
+        self.desc = make_desc(wl.d, wl.E, wl.k, wl.I, wl.S, wl.renormalize, DTYPES[wl.act],
+                              DTYPES[wl.wdt], wl.pre_norm, wl.norm_eps)
+        self.x_host = S.make_tokens(wl, T)
+        self.layers = []
+        self.host0 = None
+        for layer in range(wl.n_layers):
+            h = S.make_layer(wl, layer)
+            if layer == 0:
+                self.host0 = h
+            self.layers.append(DeviceLayer(self.desc, h.w_router, h.bias, h.w_gate, h.w_up, h.w_down))
+            del h
+        self.x0 = to_device(self.x_host)
+        self.buf = [torch.empty_like(self.x0), torch.empty_like(self.x0)]
+        self.ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+        self.ws = self.layers[0].workspace(T)
+        self.lib = abi.lib()
+        stream = torch.cuda.current_stream().cuda_stream
+        self.args = []
+        for i, L in enumerate(self.layers):
+            src = self.x0 if i == 0 else self.buf[(i - 1) % 2]
+            self.args.append(_forward_args(self.desc, T, src, L, src, self.buf[i % 2], self.ws, stream))
+
+    def step(self, _i=0):
+        for a in self.args:
+            _call(self.lib, a)
+
+    def layer(self, i):
+        _call(self.lib, self.args[i % len(self.args)])
+
+    def parity_gate(self, n_tokens=8):
+        """Layer 0 on sampled tokens against the oracle fed the same bf16 input."""
+        import numpy as np
+        import torch
+
+        from grouped_expert_ffn_amd import from_device
+        from oracle import moe_oracle as O
+        wl, T = self.wl, self.T
+        self.layers[0].forward(self.x0, residual=self.x0, y=self.buf[0], topk_ids=self.ids)
+        torch.cuda.synchronize()
+        ids = self.ids.cpu().numpy()
+        tok = sorted(set(np.linspace(0, T - 1, n_tokens).astype(int).tolist()))
+        xn = O.stack_layer_input(self.x_host[tok], wl.norm_eps)
+        logits = O.router_logits(xn, self.host0.w_router, self.host0.bias)
+        w = O.gate_weights_for(logits, ids[tok], wl.renormalize)
+        ref = O.moe_layer(xn, O.Experts.from_layer(self.host0), ids[tok], w, 0, wl.E,
+                          residual=self.x_host[tok])
+        counts = np.bincount(ids.ravel(), minlength=wl.E)
+        self.skew0 = float(counts.max() / (T * wl.k / wl.E))
+        return _gate(wl, f"stack layer 0 T={T}", O.widen(from_device(self.buf[0]))[tok], ref)
+
+    def free(self):
+        import torch
+        self.layers.clear()
+        self.args.clear()
+        self.host0 = None
+        torch.cuda.empty_cache()
+
+
+def measure_stack(wl, steps):
+    from grouped_expert_ffn_amd import abi
+    st = Stack(wl, wl.tokens[0])
+    rel = st.parity_gate()
+    T, n = st.T, wl.n_layers
+    ms, _ = time_steps(st.step, steps, 2)
+    gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, st.layer, 2 * n)
+    dn_ms, _ = time_kernel(abi.MOE_KERNEL_DOWN, st.layer, 2 * n)
+    work = layer_work(wl, T, wl.E)  # every expert is touched at T=2048
+    per_layer = ms / n
+    hbm, mfma = _fracs(work, per_layer)
+    res = {
+        "workload": wl.name, "tokens": T, "layers": n, "ms_per_stack": round(ms, 4),
+        "ms_per_layer": round(per_layer, 5), "tokens_per_s_per_layer": round(T / (per_layer * 1e-3), 1),
+        "layer_hbm_frac": hbm, "layer_mfma_frac": mfma,
+        "gate_up_ms": round(gu_ms, 5), "down_ms": round(dn_ms, 5),
+        "gate_up_mfma_frac": round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "down_mfma_frac": round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "busiest_over_mean_layer0": round(st.skew0, 3), "parity_rel_l2_layer0": float(f"{rel:.3e}"),
+    }
+    st.free()
+    return res
+
+
+# ------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# ------------------------------------------------------------------------------------------
 def cpu_baseline(wl, T, budget_s):
     """The fp64 oracle as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-
     import moe_synth as S
     from oracle import moe_oracle as O
     host = host_layer(wl)
@@ -280,6 +555,23 @@ def cpu_baseline(wl, T, budget_s):
                       f"per-expert loop incl. weight widening), {el:.1f} s"}
 
 
+def counters_pass(wl, T, steps, warmup, copies):
+    """What a rocprofv3 --pmc run profiles: the copy kernel whose FETCH_SIZE / WRITE_SIZE
+    calibrate the counters (256 MiB read, 256 MiB written per dispatch), then the steps."""
+    import torch
+    a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    pt = Point(wl, T, copies)
+    pt.parity_gate()
+    time_steps(pt.step, steps, warmup)
+    pt.free()
+    print(f"counters pass done: {wl.name} T={T}, {steps} steps", flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -292,7 +584,20 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     import moe_synth as S
     wl = S.WORKLOADS[args.workload]
-    res, roof, ms, wall, work = measure(wl, args.tokens, args.steps, args.warmup, args.copies)
+    if args.counters_pass:
+        counters_pass(wl, args.tokens, args.steps, args.warmup, args.copies)
+        return
+    res, roof, ms, wall, work = measure(wl, args.tokens, args.steps, args.warmup, args.copies,
+                                        extras=not args.no_extras)
+    if roof["bound"] == "hbm":
+        roof["traffic"] = read_traffic(f"gemv_gateup_{wl.name}_T{args.tokens}.pmc.txt")
+    else:
+        roof["traffic"] = read_traffic(f"gemm_gateup_{wl.name}_T{args.tokens}.pmc.txt")
+    print(f"# headline {wl.name} T={args.tokens}: {ms:.4f} ms/layer", file=sys.stderr, flush=True)
+    extras = {}
+    if not args.no_extras:
+        extras["copies_plateau_ms"] = copies_plateau(wl, args.tokens)
+        extras["copy_ceiling_gbs"] = copy_ceiling_gbs()
     sweep = []
     for item in [s for s in args.sweep.split(",") if s.strip()]:
         name, t = item.split(":")
@@ -304,6 +609,11 @@ def main():
         sweep.append(r)
         print(f"# sweep {name} T={t}: {r['ms_per_layer']:.4f} ms/layer, {r['tokens_per_s']:.0f} tok/s, "
               f"{rf['bound']} frac {rf['frac']:.3f}", file=sys.stderr, flush=True)
+    stack = None
+    if not args.no_stack:
+        stack = measure_stack(S.OLMOE_STACK16, args.stack_steps)
+        print(f"# stack: {stack['ms_per_stack']:.3f} ms / {stack['layers']} layers", file=sys.stderr,
+              flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.tokens, args.cpu_seconds)
     out = {
         "metric": "MoE-layer tokens/s (one MoE layer forward, T tokens per step)",
@@ -318,7 +628,9 @@ def main():
         "detail": res,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "extras": extras,
         "sweep": sweep,
+        "stack": stack,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
