@@ -1,7 +1,9 @@
 // Stable sort of the T*k (token, slot) rows by expert, with a block-wide prefix scan and no
 // atomics (the switchyard page sorts rows by expert this way, §02 "Route and sort").
 //
-// One workgroup of 16 wavefronts.  Wavefront w owns a contiguous range of flat rows, walked
+// One workgroup of 16 wavefronts.  The expert ids are first staged in LDS (every thread
+// issues all of its loads before the first store, so the staging costs one memory round
+// trip rather than one per step; the fused kernel writes them there from its top-k).  Wavefront w owns a contiguous range of flat rows, walked
 // 64 at a time.  Inside a step, lanes holding the same expert id find each other with eight
 // ballots (one per bit of the id); the lowest such lane is the group's leader and the rank
 // of a lane among its peers is a popcount of the lower peers.  Pass 1 builds a per-wavefront
@@ -11,9 +13,14 @@
 // ascending ranges and lanes are ranked in order, rows of one expert keep ascending flat
 // index: the sort is stable and its result unique.
 //
-// The same kernel writes the launch plan of the grouped FFN: the ascending list of groups
-// that have rows (touched routed experts, then the shared experts) and, for the MFMA path,
-// the list of (group, first row) M-tiles.
+// Past kSingleMaxRows rows the sort is spread over workgroups of kPermChunk rows each: a
+// first kernel writes every chunk's expert histogram, and the sort kernel then runs once per
+// chunk, taking its chunk's base for each expert from the histograms of the chunks before it
+// (the same offsets the one-workgroup kernel computes, so the result is identical).
+//
+// The sort kernel (its first workgroup) also writes the launch plan of the grouped FFN: the
+// ascending list of groups that have rows (touched routed experts, then the shared experts)
+// and, for the MFMA path, the list of (group, first row) M-tiles.
 #include "moe_internal.h"
 #include "topk.h"
 
@@ -24,6 +31,10 @@ namespace {
 constexpr int kPermWaves = 16;
 constexpr int kMaxGroups = 256 + 8;
 constexpr int kFusedMaxRows = 2048;  // T*k limit of the fused top-k + sort kernel
+constexpr int kSingleMaxRows = 4096;  // T*k up to which one workgroup sorts every row
+constexpr int kStageLoads = kSingleMaxRows / (kPermWaves * kWave);  // staging loads per thread
+static_assert(kFusedMaxRows <= kSingleMaxRows, "the fused kernel sorts in one workgroup");
+static_assert(kPermChunk == kPermWaves * kWave, "one 64-row step per wavefront and chunk");
 
 __device__ __forceinline__ uint64_t peer_mask(int key, bool valid) {
   uint64_t peers = __ballot(valid);
@@ -47,28 +58,56 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm,
                                                   int32_t* __restrict__ inv_perm,
-                                                  int32_t* __restrict__ plan) {
+                                                  int32_t* __restrict__ plan,
+                                                  const int32_t* __restrict__ chunk_hist) {
   __shared__ int hist[kPermWaves][256];
+  __shared__ int pre[kMaxGroups];
   __shared__ int cnt[kMaxGroups];
   __shared__ int base[kMaxGroups];
   __shared__ int touched[kMaxGroups];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int n_routed_touched;
-  __shared__ int keys_lds[FUSED ? kFusedMaxRows : 1];
+  __shared__ int keys_lds[kSingleMaxRows];  // expert ids of rows r0..r1-1
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int N = T * k;
-  const int per_wave = ((N + kPermWaves * kWave - 1) / (kPermWaves * kWave)) * kWave;
-  const int begin = wave * per_wave, end = min(N, begin + per_wave);
+  // rows [r0, r1) of this workgroup: all of them, or chunk blockIdx.x of the multi-workgroup sort
+  const bool multi = chunk_hist != nullptr;
+  const int r0 = multi ? blockIdx.x * kPermChunk : 0;
+  const int r1 = multi ? min(N, r0 + kPermChunk) : N;
+  const int nrows = r1 - r0;
+  const int per_wave = ((nrows + kPermWaves * kWave - 1) / (kPermWaves * kWave)) * kWave;
+  const int begin = r0 + wave * per_wave, end = min(r1, begin + per_wave);
+  const bool lead_block = blockIdx.x == 0;  // writes counts, offsets and the plan
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   for (int e = lane; e < 256; e += kWave) hist[wave][e] = 0;
   if (FUSED) {
-    for (int t = wave; t < T; t += kPermWaves)
-      topk_token(logits + (size_t)t * E, E, k, renorm, lane, ids, topk_w, t, keys_lds);
+    // the next token's logits are loaded while the current token is selected
+    float cur[4], nxt[4];
+    if (wave < T) topk_load(logits + (size_t)wave * E, E, lane, cur);
+    for (int t = wave; t < T; t += kPermWaves) {
+      const int tn = t + kPermWaves;
+      if (tn < T) topk_load(logits + (size_t)tn * E, E, lane, nxt);
+      topk_select(cur, E, k, renorm, lane, ids, topk_w, t, keys_lds);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+    }
+  } else {
+    int v[kStageLoads];
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int i = tid + j * kPermWaves * kWave;
+      v[j] = i < nrows ? ids[r0 + i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int i = tid + j * kPermWaves * kWave;
+      if (i < nrows) keys_lds[i] = v[j];
+    }
   }
   __syncthreads();
-  auto key_of = [&](int f) { return FUSED ? keys_lds[f] : ids[f]; };
+  auto key_of = [&](int f) { return keys_lds[f - r0]; };
 
   // pass 1: per-wavefront histograms
   for (int b0 = begin; b0 < end; b0 += kWave) {
@@ -82,7 +121,8 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
   }
   __syncthreads();
 
-  // column scan over wavefronts
+  // column scan over wavefronts; the expert totals (and, for a chunk, the rows of each expert
+  // in the chunks before it) come from the chunk histograms in the multi-workgroup sort
   for (int e = tid; e < E; e += blockDim.x) {
     int run = 0;
     for (int w = 0; w < kPermWaves; ++w) {
@@ -90,7 +130,20 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
       hist[w][e] = run;
       run += c;
     }
-    cnt[e] = run;
+    if (multi) {
+      const int nb = (N + kPermChunk - 1) / kPermChunk;
+      int before = 0, total = 0;
+      for (int b = 0; b < nb; ++b) {
+        const int c = chunk_hist[(size_t)b * E + e];
+        before += b < (int)blockIdx.x ? c : 0;
+        total += c;
+      }
+      pre[e] = before;
+      cnt[e] = total;
+    } else {
+      pre[e] = 0;
+      cnt[e] = run;
+    }
   }
   __syncthreads();
 
@@ -119,15 +172,17 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       if (e < E) {
-        base[e] = ex;
-        counts[e] = c[i];
-        offsets[e] = ex;
+        base[e] = ex + pre[e];
+        if (lead_block) {
+          counts[e] = c[i];
+          offsets[e] = ex;
+        }
         if (c[i] > 0) touched[exf++] = e;
         ex += c[i];
       }
     }
     if (lane == kWave - 1) n_routed_touched = inclf;
-    if (lane <= S) offsets[E + lane] = N + lane * T;
+    if (lead_block && lane <= S) offsets[E + lane] = N + lane * T;
   }
   __syncthreads();
 
@@ -157,7 +212,8 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
     if (valid && lane == leader) hist[wave][key] = hist[wave][key] + __popcll(peers);
   }
 
-  // plan: touched groups and M-tiles
+  // plan: touched groups and M-tiles (first workgroup only)
+  if (!lead_block) return;
   int32_t* tl = plan + kPlanHeader;
   for (int i = tid; i < n_groups; i += blockDim.x) tl[i] = touched[i];
   if (tile_m > 0) {
@@ -212,15 +268,49 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
   }
 }
 
+// Expert histogram of each chunk of kPermChunk rows (one 64-row step per wavefront), summed
+// over the wavefronts in a fixed order.  grid: ceil(T*k / kPermChunk); block 1024
+__global__ __launch_bounds__(1024) void k_perm_hist(int N, int E, const int32_t* __restrict__ ids,
+                                                    int32_t* __restrict__ chunk_hist) {
+  __shared__ int hist[kPermWaves][256];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  for (int e = lane; e < 256; e += kWave) hist[wave][e] = 0;
+  const int f = blockIdx.x * kPermChunk + tid;
+  const bool valid = f < N;
+  int key = valid ? ids[f] : 0;
+  key = ((unsigned)key < (unsigned)E) ? key : E - 1;
+  __syncthreads();
+  const uint64_t peers = peer_mask(key, valid);
+  const int leader = __ffsll((long long)peers) - 1;
+  if (valid && lane == leader) hist[wave][key] += __popcll(peers);
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < kPermWaves; ++w) run += hist[w][e];
+    chunk_hist[(size_t)blockIdx.x * E + e] = run;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* plan,
                           int tile_m, hipStream_t s) {
+  const int N = T * L.k;
+  int32_t* idsm = const_cast<int32_t*>(ids);
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
-  k_permute<false><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr,
-                                      const_cast<int32_t*>(ids), counts, offsets, perm, inv_perm,
-                                      plan);
+  if (N <= kSingleMaxRows) {
+    k_permute<false><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
+                                        offsets, perm, inv_perm, plan, nullptr);
+    return hipGetLastError();
+  }
+  // the timer brackets both launches: it records its start before the first and its stop
+  // after the last launch made while it is alive
+  int32_t* chunk_hist = plan + plan_hist_offset(T, L.k, L.E, L.S);
+  const int nb = (N + kPermChunk - 1) / kPermChunk;
+  k_perm_hist<<<nb, 1024, 0, s>>>(N, L.E, ids, chunk_hist);
+  k_permute<false><<<nb, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
+                                       offsets, perm, inv_perm, plan, chunk_hist);
   return hipGetLastError();
 }
 
@@ -231,7 +321,7 @@ hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, i
                                int32_t* inv_perm, int32_t* plan, int tile_m, hipStream_t s) {
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
   k_permute<true><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, logits, L.renorm, topk_w, ids,
-                                     counts, offsets, perm, inv_perm, plan);
+                                     counts, offsets, perm, inv_perm, plan, nullptr);
   return hipGetLastError();
 }
 

@@ -8,17 +8,16 @@
 // prefetches the next expert's row while reducing the current one.
 //
 // Top-k: one wavefront per token (the switchyard page routes each token in one warp, §02
-// "Route and sort").  Each lane holds up to four logits as 64-bit keys (order-preserving fp32
-// bits above the inverted expert id, so keys are distinct and ties go to the lower id); the
-// rank of every key is counted against all others broadcast by readlane, and the keys of rank
-// < k are the slots, largest first.  The softmax runs over all E logits; sums and the max use
-// DPP trees in a fixed order.
+// "Route and sort").  Each lane holds up to four logits; k rounds of wave-wide max / min
+// reductions pick the slots, largest first, equal logits going to the lower expert id.  The
+// softmax runs over all E logits; sums and the max use DPP trees in a fixed order.
 #include "moe_internal.h"
 #include "topk.h"
 
 namespace moe {
 
 constexpr int kRouteTB = 8;  // tokens per router block (upper bound)
+constexpr int kRouterMfmaMinT = 64;  // the matrix-core router serves T above this
 
 namespace {
 
@@ -104,6 +103,71 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
   }
 }
 
+// Router logits on the matrix cores, for bf16 layers past decode sizes (E <= 64, d a multiple
+// of 32).  A block owns 16 tokens and all experts; its 8 wavefronts split K into 8 contiguous
+// slices and each accumulates the 16 x 16*NJ partial logits of its slice with
+// v_mfma_f32_16x16x32_bf16, reading both operands straight from global memory (x rows once,
+// the 256 KiB router matrix from L2).  The eight partials are summed in LDS in a fixed order.
+// grid: ceil(T / 16); block 512
+constexpr int kRouterMfmaWaves = 8;
+template <int NJ>
+__global__ __launch_bounds__(512) void k_router_mfma(int T, int d, int E,
+                                                     const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ w,
+                                                     const float* __restrict__ bias,
+                                                     float* __restrict__ logits) {
+  __shared__ float red[kRouterMfmaWaves][16][16 * NJ];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int t0 = blockIdx.x * 16;
+  const int lr = lane % 16, kc = (lane / 16) * 8;
+  const int steps = d / 32;
+  const int s0 = wave * steps / kRouterMfmaWaves, s1 = (wave + 1) * steps / kRouterMfmaWaves;
+  // rows past T or E are clamped (their results are discarded)
+  const uint16_t* xr = x + (size_t)min(t0 + lr, T - 1) * d + kc;
+  const uint16_t* wr[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) wr[j] = w + (size_t)min(16 * j + lr, E - 1) * d + kc;
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // K-steps in batches of U: all loads of a batch are issued before its first MFMA.  A tail
+  // batch re-reads its last step and zeroes that step's activations, so the duplicate adds 0.
+  constexpr int U = 4;
+  const bf16x8 zero = {};
+  for (int sb = s0; sb < s1; sb += U) {
+    bf16x8 a[U], b[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = min(sb + u, s1 - 1) * 32;
+      a[u] = *reinterpret_cast<const bf16x8*>(xr + kk);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[u][j] = *reinterpret_cast<const bf16x8*>(wr[j] + kk);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its MFMAs
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bf16x8 au = sb + u < s1 ? a[u] : zero;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, b[u][j], acc[j], 0, 0, 0);
+    }
+  }
+  // lane holds tokens 4*(lane/16) + v of expert 16*j + lane%16
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][(lane / 16) * 4 + v][16 * j + lr] = acc[j][v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * 16 * NJ; i += blockDim.x) {
+    const int tt = i / (16 * NJ), e = i % (16 * NJ);
+    if (t0 + tt < T && e < E) {
+      const float sum = ((red[0][tt][e] + red[1][tt][e]) + (red[2][tt][e] + red[3][tt][e])) +
+                        ((red[4][tt][e] + red[5][tt][e]) + (red[6][tt][e] + red[7][tt][e]));
+      logits[(size_t)(t0 + tt) * E + e] = sum + (bias ? bias[e] : 0.f);
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -115,7 +179,9 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int k, int renorm,
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  topk_token(logits + (size_t)t * E, E, k, renorm, lane, ids, wout, t, nullptr);
+  float l[4];
+  topk_load(logits + (size_t)t * E, E, lane, l);
+  topk_select(l, E, k, renorm, lane, ids, wout, t, nullptr);
 }
 
 // y = x / sqrt(mean(x^2) + eps), one block per token, fp32 sums in a fixed order
@@ -151,8 +217,26 @@ hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, fl
   return hipGetLastError();
 }
 
+// Matrix-core router: bf16, at most 64 experts, K in whole MFMA steps, past decode sizes.
+static bool router_on_mfma(const LayerDims& L, int T) {
+  return L.act == MOE_BF16 && L.E <= 64 && L.d % 32 == 0 && T > kRouterMfmaMinT;
+}
+
 hipError_t launch_router_logits(const LayerDims& L, int T, const void* x, const void* w_router,
                                 const float* bias, float* logits, hipStream_t s) {
+  if (router_on_mfma(L, T)) {
+    const dim3 grid((T + 15) / 16);
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* wb = (const uint16_t*)w_router;
+    LaunchTimer timer(MOE_KERNEL_ROUTER, s);
+    switch ((L.E + 15) / 16) {
+      case 1: k_router_mfma<1><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
+      case 2: k_router_mfma<2><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
+      case 3: k_router_mfma<3><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
+      default: k_router_mfma<4><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
+    }
+    return hipGetLastError();
+  }
   const int esz = L.act == MOE_F32 ? 4 : 2;
   int tb = kRouteTB;
   while (tb > 1 && (size_t)tb * L.d * esz > 64 * 1024) tb >>= 1;

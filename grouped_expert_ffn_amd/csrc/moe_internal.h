@@ -126,14 +126,20 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 //   [3] reserved
 //   [4 .. 4+E+S)            touched group ids, ascending (routed first, then shared)
 //   [4+E+S .. + 2*max_tiles) tile list: (group, first row within the group)
+//   then, for the multi-workgroup sort, one expert histogram per chunk of kPermChunk rows
 constexpr int kPlanHeader = 4;
 constexpr int kMinTileM = 16;
+constexpr int kPermChunk = 1024;  // rows per workgroup of the multi-workgroup sort
 inline size_t plan_max_tiles(int T, int k, int E, int S) {
   const size_t N = (size_t)T * k;
   return N / kMinTileM + (size_t)E + (size_t)S * ((T + kMinTileM - 1) / kMinTileM) + 1;
 }
-inline size_t plan_words(int T, int k, int E, int S) {
+inline size_t plan_hist_offset(int T, int k, int E, int S) {
   return kPlanHeader + (size_t)(E + S) + 2 * plan_max_tiles(T, k, E, S);
+}
+inline size_t plan_words(int T, int k, int E, int S) {
+  const size_t chunks = ((size_t)T * k + kPermChunk - 1) / kPermChunk;
+  return plan_hist_offset(T, k, E, S) + chunks * (size_t)E;
 }
 
 // -------------------------------------------------------------------------------------

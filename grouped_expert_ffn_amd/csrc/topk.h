@@ -1,4 +1,11 @@
 // Top-k gating of one token by one wavefront; shared by the top-k and fused permute kernels.
+//
+// Lane l holds the logits of experts l, l+64, l+128 and l+192 (E <= 256), each with an
+// order-preserving 32-bit code (NaN lowest).  The k slots are filled in k rounds: every lane
+// offers its best remaining expert (highest code, then lowest id), a wave-wide max over the
+// offers picks the code, a wave-wide min over the lanes offering that code picks the lowest
+// id, and that expert leaves the pool.  Slots are therefore ordered by descending logit,
+// equal logits go to the lower expert id, and NaN ranks below every number.
 #pragma once
 
 #include "moe_internal.h"
@@ -13,42 +20,75 @@ __device__ __forceinline__ uint32_t order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t readlane_u(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+// wave-wide max / min of uint32, the same in every lane (all 64 lanes must be active)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  return max(max(readlane_u(v, 0), readlane_u(v, 16)), max(readlane_u(v, 32), readlane_u(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<0xB1>(v));
+  v = min(v, dpp_u<0x4E>(v));
+  v = min(v, dpp_u<0x141>(v));
+  v = min(v, dpp_u<0x140>(v));
+  return min(min(readlane_u(v, 0), readlane_u(v, 16)), min(readlane_u(v, 32), readlane_u(v, 48)));
 }
 
-// Top-k gating of token t by one whole wavefront (all 64 lanes active).  Writes ids/w of
-// the token's k slots; when keys_lds is given, the ids are also written there at t*k + slot.
-__device__ __forceinline__ void topk_token(const float* __restrict__ lrow, int E, int k, int renorm, int lane,
-                           int32_t* __restrict__ ids, float* __restrict__ wout, int t,
-                           int* keys_lds) {
-  float l[4];
-  uint64_t key[4];
+// The token's logits into the lane's four slots (-inf past E).  All four loads are issued
+// unconditionally (clamped to the row), so they are in flight together.
+__device__ __forceinline__ void topk_load(const float* __restrict__ lrow, int E, int lane, float (&l)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
-    if (e < E) {
-      l[i] = lrow[e];
-      key[i] = ((uint64_t)order_bits(l[i]) << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
-    } else {
-      l[i] = -INFINITY;
-      key[i] = 0;
-    }
+    const float v = lrow[min(e, E - 1)];
+    l[i] = e < E ? v : -INFINITY;
   }
-  // rank of each key among the E keys
-  int rank[4] = {0, 0, 0, 0};
-  const int groups = (E + kWave - 1) / kWave;
-  for (int j = 0; j < groups; ++j) {
-    const int n_src = min(kWave, E - kWave * j);
-    uint64_t kj = key[0];
+}
+
+// Top-k gating of token t from its loaded logits, by one whole wavefront (all 64 lanes
+// active).  Writes ids/w of the token's k slots; when keys_lds is given, the ids are also
+// written there at t*k + slot.
+__device__ __forceinline__ void topk_select(const float (&l)[4], int E, int k, int renorm, int lane,
+                                            int32_t* __restrict__ ids, float* __restrict__ wout, int t,
+                                            int* keys_lds) {
+  const int slots = (E + kWave - 1) / kWave;
+  uint32_t code[4];
+  bool live[4];
+  int rank[4];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) kj = (j == i) ? key[i] : kj;
-    for (int src = 0; src < n_src; ++src) {
-      const uint64_t other = readlane64(kj, src);
+  for (int i = 0; i < 4; ++i) {
+    code[i] = order_bits(l[i]);
+    live[i] = lane + kWave * i < E;
+    rank[i] = k;  // k = not chosen
+  }
+  for (int r = 0; r < k; ++r) {
+    uint32_t bc = 0u, be = 0xFFFFu;
+    bool any = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rank[i] += other > key[i];
+    for (int i = 0; i < 4; ++i) {
+      if (i < slots && live[i] && (!any || code[i] > bc)) {  // later slots have higher ids
+        bc = code[i];
+        be = (uint32_t)(lane + kWave * i);
+        any = true;
+      }
+    }
+    const uint32_t m = wave_max_u32(any ? bc : 0u);
+    const int win = (int)wave_min_u32((any && bc == m) ? be : 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < slots && live[i] && lane + kWave * i == win) {
+        live[i] = false;
+        rank[i] = r;
+      }
     }
   }
   // softmax over all E, then the k chosen weights (optionally renormalised)

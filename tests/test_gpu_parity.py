@@ -66,7 +66,11 @@ def test_topk_on_given_logits_is_bit_exact(E, k, renorm, kind):
 # ----------------------------------------------------------------------------------------
 # step 1: router GEMM
 # ----------------------------------------------------------------------------------------
-ROUTE_CASES = [(S.TINY_F32, 16), (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 64), (S.DEEPSEEK_BF16, 2048)]
+# a bf16 router whose expert count is not a multiple of the 16-expert MFMA tile
+ROUTER_E40 = S.Workload("router_e40", 94, d=320, E=40, k=4, I=32, renormalize=True,
+                        routing="zipf", router_std=320 ** -0.5, zipf_alpha=1.2, tokens=(77,))
+ROUTE_CASES = [(S.TINY_F32, 16), (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 64), (S.OLMOE_BF16, 65),
+               (S.DEEPSEEK_BF16, 2048), (ROUTER_E40, 77), (ROUTER_E40, 1000)]
 
 
 @pytest.mark.parametrize("wl,T", ROUTE_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -111,7 +115,8 @@ def ids_case(kind, T, E, k, seed):
 
 @pytest.mark.parametrize("T,E,k,S_", [(1, 8, 2, 0), (16, 8, 2, 0), (1, 64, 8, 0), (37, 64, 6, 2),
                                       (64, 64, 8, 0), (300, 256, 16, 1), (2048, 64, 8, 0),
-                                      (2048, 64, 6, 2), (1000, 3, 1, 0), (513, 64, 8, 8)])
+                                      (2048, 64, 6, 2), (1000, 3, 1, 0), (513, 64, 8, 8),
+                                      (2100, 64, 8, 0)])
 @pytest.mark.parametrize("kind", ["uniform", "same", "zipf"])
 def test_permute_is_bit_exact(T, E, k, S_, kind):
     from grouped_expert_ffn_amd import (MOE_WS_PERMUTE, alloc_workspace, make_desc, moe_permute,
