@@ -13,8 +13,11 @@
 // read in order (h rows).  128 rows keep the padding of the last tile of each expert small
 // under skewed routing, where most experts get a few hundred rows.
 //
-//  * k_gemm_ring (bf16 weights, K a multiple of 32): 128x256 tiles, eight wavefronts in a
-//    2x4 layout each owning 64x64 (sixteen 16x16 MFMA tiles).  BK=32 and a ring of NST LDS stages
+//  * k_gemm_ring (bf16 weights, K a multiple of 32): 128x256 tiles, four wavefronts side by
+//    side each owning 128x64 (32 MFMA tiles), so a group's last, partly filled tile skips
+//    the MFMAs of its empty 16-row slices in every wavefront alike.  The weights are the
+//    first MFMA operand, which leaves 4 consecutive output channels in each lane for 8-byte
+//    stores.  BK=32 and a ring of NST LDS stages
 //    filled directly from global memory by global_load_lds_dwordx4, issued NST-1 stages
 //    ahead of the MFMAs, so several stages of loads are always in flight without holding
 //    registers.  The DMA writes lane l's 16 bytes at base + 16*l, so a stage is row-major
@@ -26,6 +29,8 @@
 //    a register prefetch of the next K-step; int8 weights are widened to bf16 (exact) on
 //    the way into LDS.  The per-channel int8 scale multiplies the fp32 accumulator in the
 //    epilogue.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -305,19 +310,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
 
-// Tile RBM x RBN (gate/up: RBN/2 gate + the same RBN/2 up channels), WM x WN wavefronts,
-// each owning (RBM/WM) x (RBN/WN); K advances RBK=32 per stage through an RNST-deep ring.
-constexpr int RBM = 128, RBN = 256, RWM = 2, RWN = 4;
-constexpr int R_THREADS = 64 * RWM * RWN;
-constexpr int R_TI = RBM / RWM / 16, R_TJ = RBN / RWN / 16;  // 16x16 MFMA tiles per wavefront
+// Tile RBM x RBN (gate/up: RBN/2 gate + the same RBN/2 up channels); four wavefronts side by
+// side, each owning all RBM rows and RBN/4 columns (gate/up: RBN/8 gate + the same up
+// channels); K advances RBK=32 per stage through an RNST-deep ring.
+constexpr int RBM = 128, RBN = 256, RWN = 4;
+constexpr int R_THREADS = 64 * RWN;
+constexpr int R_TI = RBM / 16, R_TJ = RBN / RWN / 16;  // 16x16 MFMA tiles per wavefront
 constexpr int R_A_BYTES = RBM * RBK * 2, R_STAGE = (RBM + RBN) * RBK * 2;
-constexpr int R_DMA_A = RBM / 16 / (RWM * RWN), R_DMA_B = RBN / 16 / (RWM * RWN);  // per wave
-constexpr int R_LPS = R_DMA_A + R_DMA_B;  // loads per stage per wavefront
+constexpr int R_DMA_A = RBM / 16 / RWN, R_DMA_B = RBN / 16 / RWN;  // loads per stage per wave
+constexpr int R_LPS = R_DMA_A + R_DMA_B;
 constexpr size_t R_LDS = (size_t)RNST * R_STAGE;
 static_assert((RNST - 2) * R_LPS < 16, "vmcnt range");
 
 template <int MODE>
-__global__ __launch_bounds__(R_THREADS) void k_gemm_ring(const GemmArgs a) {
+__global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_ring(
+    const GemmArgs a) {
   extern __shared__ __align__(16) unsigned char rlds[];
   Work w;
   if (!map_work_t<RBM>(a, w)) return;
@@ -357,14 +364,13 @@ __global__ __launch_bounds__(R_THREADS) void k_gemm_ring(const GemmArgs a) {
                                        0, 0);
   };
 
-  const int wm = wave / RWN, wn = wave % RWN;
-  const int lr = lane % 16;
+  const int wn = wave, lr = lane % 16;
   // operand reads: row r (a multiple of 16 plus lr), logical chunk c = lane/16 -> byte
   // offset r*64 + ((c ^ swz(r)) * 16); swz(r) = (lr >> 2) & 3 since r - lr is a multiple of 16
   const int rd_chunk = ((lane / 16) ^ ((lr >> 2) & 3)) * 16;
   int a_off[R_TI], b_off[R_TJ];
 #pragma unroll
-  for (int i = 0; i < R_TI; ++i) a_off[i] = (wm * (RBM / RWM) + i * 16 + lr) * 64 + rd_chunk;
+  for (int i = 0; i < R_TI; ++i) a_off[i] = (i * 16 + lr) * 64 + rd_chunk;
 #pragma unroll
   for (int j = 0; j < R_TJ; ++j) {
     int row;
@@ -374,7 +380,12 @@ __global__ __launch_bounds__(R_THREADS) void k_gemm_ring(const GemmArgs a) {
       row = wn * (RBN / RWN) + j * 16 + lr;
     b_off[j] = R_A_BYTES + row * 64 + rd_chunk;
   }
+  // 16-row slices of the tile that hold rows of the group; the MFMAs of the others (the
+  // padding of a group's last tile) are skipped
+  const int ni = min(R_TI, (w.M - w.m0 + 15) / 16);
 
+  // acc[i][j] is the transposed 16x16 product (weights as the first operand), so each lane
+  // ends up with 4 consecutive output channels of one row
   f32x4 acc[R_TI][R_TJ];
 #pragma unroll
   for (int i = 0; i < R_TI; ++i)
@@ -385,54 +396,76 @@ __global__ __launch_bounds__(R_THREADS) void k_gemm_ring(const GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < RNST - 1; ++s)
     if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt is complete once at most (stages issued after it) * R_LPS loads are pending
-    const int ahead = min(nk - 1, kt + RNST - 2) - kt;
-    if (ahead >= 2)
-      wait_vmcnt<2 * R_LPS>();
-    else if (ahead == 1)
-      wait_vmcnt<R_LPS>();
-    else
-      wait_vmcnt<0>();
-    // Every wavefront waited for its own loads of stage kt above, so after this barrier the
-    // whole stage is in LDS and every wavefront is done with stage kt-1.  A plain s_barrier:
-    // __syncthreads() would add a release fence, i.e. wait for all loads in flight.
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + RNST - 1 < nk) issue(kt + RNST - 1);
-    const unsigned char* st = rlds + (kt % RNST) * R_STAGE;
-    bf16x8 bfr[R_TJ];
+  // the K loop, instantiated per number of live 16-row slices so that it has no branches
+  auto k_loop = [&](auto live) {
+    constexpr int NI = decltype(live)::value;
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt is complete once at most (stages issued after it) * R_LPS loads are pending
+      const int ahead = min(nk - 1, kt + RNST - 2) - kt;
+      if (ahead >= 2)
+        wait_vmcnt<2 * R_LPS>();
+      else if (ahead == 1)
+        wait_vmcnt<R_LPS>();
+      else
+        wait_vmcnt<0>();
+      // Every wavefront waited for its own loads of stage kt above, so after this barrier the
+      // whole stage is in LDS and every wavefront is done with stage kt-1.  A plain
+      // s_barrier: __syncthreads() would add a release fence, i.e. wait for all loads in flight.
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + RNST - 1 < nk) issue(kt + RNST - 1);
+      const unsigned char* st = rlds + (kt % RNST) * R_STAGE;
+      bf16x8 bfr[R_TJ], af[NI];
 #pragma unroll
-    for (int j = 0; j < R_TJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
+      for (int j = 0; j < R_TJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
 #pragma unroll
-    for (int i = 0; i < R_TI; ++i) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
+      for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
 #pragma unroll
-      for (int j = 0; j < R_TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < R_TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
+  };
+  static_assert(R_TI == 8, "one K-loop instance per live-slice count");
+  switch (ni) {
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    case 4: k_loop(std::integral_constant<int, 4>{}); break;
+    case 5: k_loop(std::integral_constant<int, 5>{}); break;
+    case 6: k_loop(std::integral_constant<int, 6>{}); break;
+    case 7: k_loop(std::integral_constant<int, 7>{}); break;
+    default: k_loop(std::integral_constant<int, 8>{}); break;
   }
 
-  // epilogue: lane holds rows 4*(lane/16) + v, column lane%16 of each 16x16 tile
+  // epilogue: lane holds output channels 4*(lane/16) + v (v = 0..3) of tile row lane%16;
+  // they are written as one 8-byte store per row and tile
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   const int N = a.N;
+  const int c4 = 4 * (lane / 16);
 #pragma unroll
   for (int i = 0; i < R_TI; ++i) {
+    const int m = w.m0 + i * 16 + lr;
+    if (m >= w.M) continue;
+    uint16_t* orow = out + (size_t)(w.r0 + m) * N;
+    if (MODE == 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = w.m0 + wm * (RBM / RWM) + i * 16 + (lane / 16) * 4 + v;
-      if (m >= w.M) continue;
-      const size_t orow = (size_t)(w.r0 + m) * N;
-      if (MODE == 0) {
-#pragma unroll
-        for (int j = 0; j < R_TJ / 2; ++j) {
-          const int n = w.n0 + wn * (RBN / RWN / 2) + j * 16 + lr;
-          if (n < N) out[orow + n] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + R_TJ / 2][v]);
+      for (int j = 0; j < R_TJ / 2; ++j) {
+        const int n = w.n0 + wn * (RBN / RWN / 2) + j * 16 + c4;  // N % 16 == 0: all 4 or none
+        if (n < N) {
+          const f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
+          *reinterpret_cast<uint2*>(orow + n) =
+              make_uint2(pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
+                         pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]));
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < R_TJ; ++j) {
-          const int n = w.n0 + wn * (RBN / RWN) + j * 16 + lr;
-          if (n < N) out[orow + n] = f32_to_bf16(acc[i][j][v]);
+      for (int j = 0; j < R_TJ; ++j) {
+        const int n = w.n0 + wn * (RBN / RWN) + j * 16 + c4;
+        if (n < N) {
+          const f32x4 o = acc[i][j];
+          *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
       }
     }
