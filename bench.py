@@ -97,9 +97,11 @@ def layer_work(wl, T, n_touched_routed):
     }
 
 
-def mfma_bound(wl, T):
-    """The prefill regime: bf16 layers at T >= 512 are priced against the matrix peak."""
-    return T >= 512 and wl.act == "bf16"
+def mfma_bound(wl, T, work):
+    """Whether a layer's gate/up kernel is bound by the matrix cores rather than by HBM:
+    its flops at the bf16 peak take longer than its algorithmic bytes at the HBM peak."""
+    return (wl.act == "bf16" and work["gate_up_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+            > work["gate_up_bytes"] / (HBM_PEAK_GBS * 1e9))
 
 
 # ------------------------------------------------------------------------------------------
@@ -365,16 +367,21 @@ def _gate(wl, what, got, ref):
 
 
 def roofline_for(wl, T, work, kern_ms, traffic=None):
-    if mfma_bound(wl, T):
-        achieved = work["gate_up_flops"] / (kern_ms * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": "grouped gate/up + SwiGLU (MFMA)", "achieved": round(achieved, 1),
-                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                "traffic": traffic, "flops_per_launch": work["gate_up_flops"],
-                "avg_launch_ms": round(kern_ms, 5)}
-    achieved = work["gate_up_bytes"] / (kern_ms * 1e-3) / 1e9
-    return {"bound": "hbm", "kernel": "grouped gate/up + SwiGLU (GEMV)", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "bytes_per_launch": work["gate_up_bytes"], "avg_launch_ms": round(kern_ms, 5)}
+    """Roofline of the gate/up kernel: its algorithmic bytes against the HBM peak and its
+    flops against the bf16 matrix peak; the bound is whichever takes longer at peak, and
+    frac is that time over the measured launch time."""
+    gemm = T > 32 and wl.act == "bf16"
+    name = "grouped gate/up + SwiGLU (" + ("MFMA GEMM" if gemm else "GEMV") + ")"
+    hbm = work["gate_up_bytes"] / (kern_ms * 1e-3) / 1e9
+    mfma = work["gate_up_flops"] / (kern_ms * 1e-3) / 1e12
+    common = {"kernel": name, "traffic": traffic, "bytes_per_launch": work["gate_up_bytes"],
+              "flops_per_launch": work["gate_up_flops"], "avg_launch_ms": round(kern_ms, 5),
+              "hbm_frac": round(hbm / HBM_PEAK_GBS, 4), "mfma_frac": round(mfma / MFMA_BF16_PEAK_TFS, 4)}
+    if mfma_bound(wl, T, work):
+        return {"bound": "mfma", "achieved": round(mfma, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(mfma / MFMA_BF16_PEAK_TFS, 4), **common}
+    return {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), **common}
 
 
 def _fracs(work, ms):
@@ -405,7 +412,7 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         "down_hbm_frac": round(work["down_bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "touched_experts": n_touched, "parity_rel_l2": float(f"{rel:.3e}"),
     }
-    if mfma_bound(wl, T):
+    if T > 32 and wl.act == "bf16":
         res["gate_up_mfma_frac"] = round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
         res["down_mfma_frac"] = round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
     if extras:
@@ -589,10 +596,8 @@ def main():
         return
     res, roof, ms, wall, work = measure(wl, args.tokens, args.steps, args.warmup, args.copies,
                                         extras=not args.no_extras)
-    if roof["bound"] == "hbm":
-        roof["traffic"] = read_traffic(f"gemv_gateup_{wl.name}_T{args.tokens}.pmc.txt")
-    else:
-        roof["traffic"] = read_traffic(f"gemm_gateup_{wl.name}_T{args.tokens}.pmc.txt")
+    kind = "gemm" if "GEMM" in roof["kernel"] else "gemv"
+    roof["traffic"] = read_traffic(f"{kind}_gateup_{wl.name}_T{args.tokens}.pmc.txt")
     print(f"# headline {wl.name} T={args.tokens}: {ms:.4f} ms/layer", file=sys.stderr, flush=True)
     extras = {}
     if not args.no_extras:
