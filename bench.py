@@ -370,7 +370,7 @@ def roofline_for(wl, T, work, kern_ms, traffic=None):
     """Roofline of the gate/up kernel: its algorithmic bytes against the HBM peak and its
     flops against the bf16 matrix peak; the bound is whichever takes longer at peak, and
     frac is that time over the measured launch time."""
-    gemm = T > 32 and wl.act == "bf16"
+    gemm = T > 8 and wl.act == "bf16"
     name = "grouped gate/up + SwiGLU (" + ("MFMA GEMM" if gemm else "GEMV") + ")"
     hbm = work["gate_up_bytes"] / (kern_ms * 1e-3) / 1e9
     mfma = work["gate_up_flops"] / (kern_ms * 1e-3) / 1e12
@@ -412,7 +412,7 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         "down_hbm_frac": round(work["down_bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "touched_experts": n_touched, "parity_rel_l2": float(f"{rel:.3e}"),
     }
-    if T > 32 and wl.act == "bf16":
+    if T > 8 and wl.act == "bf16":
         res["gate_up_mfma_frac"] = round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
         res["down_mfma_frac"] = round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
     if extras:

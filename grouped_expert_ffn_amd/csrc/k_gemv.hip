@@ -280,7 +280,7 @@ hipError_t dispatch_gemv(const GemvArgs& a, int slots, hipStream_t s) {
   const int steps = (a.K + 8 * V - 1) / (8 * V);
   const int spw = (steps + kWaves - 1) / kWaves;
   if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 8), 2>(a, slots, s);
-  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 2 : 4), 4>(a, slots, s);
+  if (spw <= 4) return run_gemv<MODE, AT, WT, 2, 4>(a, slots, s);
   return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8>(a, slots, s);
 }
 

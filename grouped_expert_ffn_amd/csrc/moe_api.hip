@@ -141,9 +141,14 @@ LaunchTimer::~LaunchTimer() {
   if (stop_) (void)hipEventRecord((hipEvent_t)stop_, s_);
 }
 
+constexpr int kGemvMaxTokens = 8;
+
 int ffn_tile_m(const LayerDims& L, int T) {
   if (L.act == MOE_F32) return 0;
-  return T > 32 ? gemm_tile_m(L) : 0;
+  // The GEMV streams each group's weights once and does its rows in passes of up to 8;
+  // past 8 tokens some group (a shared expert, a heavy expert under skewed routing) needs
+  // several passes and the matrix-core GEMM is faster (measured at T = 16 and 32).
+  return T > kGemvMaxTokens ? gemm_tile_m(L) : 0;
 }
 
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s) {
