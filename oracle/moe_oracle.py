@@ -28,14 +28,20 @@ What the layer computes, from the pages:
   (dispatch README, "Stack");
 * int8 weight-only experts are per-channel quantised and dequantised inside
   the kernel (dispatch README, "What has been measured", phase 5a);
-* no token is ever dropped (switchyard §03 "Load balance": dropless).
+* no token is dropped by default (switchyard §03 "Load balance": dropless);
+  as an option, a capacity limit drops the rows an expert has no room for
+  (the same section, "What dropping tokens costs": capacity factors 2.0 and
+  1.0 against dropless).
 
 Readings taken where the pages are silent (each is listed in the design doc):
 softmax over all E logits, then top-k, then optional renormalisation; the
 selection is made on the logits (softmax is strictly increasing, so this is
 the same set), largest first, equal logits going to the lower expert id, NaN
 ranking below every number; shared experts carry weight 1 and come after the
-routed slots; the RMSNorm of the stacked workload has no learned scale.
+routed slots; the RMSNorm of the stacked workload has no learned scale; with a
+capacity factor cf each routed expert keeps ceil(cf*T*k/E) rows, the earliest
+(token, slot) pairs in flat order t*k+j, a dropped pair contributes nothing
+(the remaining gate weights are not rescaled) and shared experts never drop.
 """
 from __future__ import annotations
 
@@ -166,6 +172,52 @@ def permute(ids: np.ndarray, n_experts: int):
 
 
 # --------------------------------------------------------------------------
+# option: capacity-factor dropping (switchyard §03 "Load balance", "What
+# dropping tokens costs")
+# --------------------------------------------------------------------------
+def capacity(capacity_factor: float, T: int, k: int, n_experts: int) -> int:
+    """Rows each routed expert may keep: ``ceil(cf * T * k / E)``; 0 = no limit.
+
+    The factor is taken as the float32 value the library receives, and the
+    product is formed in double precision in the order ((cf * T) * k) / E."""
+    cf = float(np.float32(capacity_factor))
+    if not cf > 0.0:
+        return 0
+    return int(math.ceil(cf * T * k / n_experts))
+
+
+def kept_slots(ids: np.ndarray, n_experts: int, cap: int) -> np.ndarray:
+    """``keep[t, j]``: whether slot j of token t finds room in its expert.
+
+    The (token, slot) pairs are visited in flat order ``t*k + j`` and each
+    expert accepts the first ``cap`` pairs that reach it (no limit if cap is 0).
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    keep = np.ones((T, k), dtype=bool)
+    if cap <= 0:
+        return keep
+    seen = [0] * n_experts
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            keep[t, j] = seen[e] < cap
+            seen[e] += 1
+    return keep
+
+
+def permute_with_capacity(ids: np.ndarray, n_experts: int, cap: int):
+    """``permute`` of all rows, with ``inv_perm[f] = -1`` for every dropped pair.
+
+    Dropped pairs keep their place in the sort (they are the tail of their
+    expert's segment), so counts, offsets and perm are those of ``permute``."""
+    counts, offsets, perm, inv_perm = permute(ids, n_experts)
+    keep = kept_slots(ids, n_experts, cap).ravel()
+    inv_perm = np.where(keep, inv_perm, -1)
+    return counts, offsets, perm, inv_perm
+
+
+# --------------------------------------------------------------------------
 # step 3/4: the expert feed-forward block
 # --------------------------------------------------------------------------
 def silu(z: np.ndarray) -> np.ndarray:
@@ -218,11 +270,13 @@ def expert_ffn(x_t: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray):
 # --------------------------------------------------------------------------
 def moe_layer(x: np.ndarray, experts: Experts, ids: np.ndarray, w: np.ndarray,
               n_shared: int, n_experts: int, residual: Optional[np.ndarray] = None,
-              tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+              tokens: Optional[Sequence[int]] = None,
+              keep: Optional[np.ndarray] = None) -> np.ndarray:
     """``y[t] = sum_j w[t,j] FFN_{ids[t,j]}(x_t) + sum_s FFN_{E+s}(x_t) (+ residual[t])``.
 
     ``tokens`` restricts the loop to a subset of tokens (rows of the result
-    follow that subset's order).
+    follow that subset's order).  ``keep[t, j]`` False drops slot j of token t
+    (the capacity option); the sum then skips it.
     """
     xf = widen(x)
     T = xf.shape[0]
@@ -232,6 +286,8 @@ def moe_layer(x: np.ndarray, experts: Experts, ids: np.ndarray, w: np.ndarray,
     for i, t in enumerate(sel):
         acc = np.zeros(xf.shape[1], dtype=np.float64)
         for j in range(ids.shape[1]):
+            if keep is not None and not keep[t, j]:
+                continue
             o, _ = expert_ffn(xf[t], *experts.get(int(ids[t, j])))
             acc += w[t, j] * o
         for s in range(n_shared):
@@ -298,7 +354,9 @@ def sorted_rows(x: np.ndarray, experts: Experts, ids: np.ndarray, perm: np.ndarr
 
 def combine(rows: np.ndarray, inv_perm: np.ndarray, w: np.ndarray, n_shared: int,
             residual: Optional[np.ndarray] = None) -> np.ndarray:
-    """``y[t] = sum_j w[t,j] rows[inv_perm[t*k+j]] + sum_s rows[T*k + s*T + t] (+ residual[t])``."""
+    """``y[t] = sum_j w[t,j] rows[inv_perm[t*k+j]] + sum_s rows[T*k + s*T + t] (+ residual[t])``.
+
+    A pair with ``inv_perm < 0`` was dropped by the capacity option and adds nothing."""
     rf = widen(rows)
     T, k = w.shape
     out = np.zeros((T, rf.shape[1]), dtype=np.float64)
@@ -306,7 +364,9 @@ def combine(rows: np.ndarray, inv_perm: np.ndarray, w: np.ndarray, n_shared: int
     for t in range(T):
         acc = np.zeros(rf.shape[1], dtype=np.float64)
         for j in range(k):
-            acc += w[t, j] * rf[int(inv_perm[t * k + j])]
+            r = int(inv_perm[t * k + j])
+            if r >= 0:
+                acc += w[t, j] * rf[r]
         for s in range(n_shared):
             acc += rf[T * k + s * T + t]
         if res is not None:

@@ -408,3 +408,84 @@ def test_round_to_bf16_ties_and_pattern():
     # every result has at most 8 significant bits
     m, _ = np.frexp(v)
     assert np.all(m * 256 == np.rint(m * 256))
+
+
+# --------------------------------------------------------------------------
+# option: capacity-factor dropping
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cf,T,k,E,C", [
+    (1.0, 2048, 8, 64, 256),   # exactly T*k/E
+    (2.0, 2048, 8, 64, 512),
+    (2.0, 16, 2, 8, 8),
+    (1.25, 10, 3, 4, 10),      # 9.375 rounds up
+    (1.0, 3, 1, 2, 2),         # 1.5 rounds up
+    (0.1, 1, 1, 64, 1),        # at least one row
+    (0.0, 100, 8, 64, 0),      # 0: no limit
+    (-1.0, 100, 8, 64, 0),
+])
+def test_capacity_closed_form(cf, T, k, E, C):
+    assert O.capacity(cf, T, k, E) == C
+
+
+def test_kept_slots_hand_example():
+    # flat order: (t0: e0 e1) (t1: e0 e2) (t2: e0 e1) (t3: e1 e0), two rows per expert
+    ids = np.array([[0, 1], [0, 2], [0, 1], [1, 0]])
+    keep = O.kept_slots(ids, 3, 2)
+    expect = np.array([[True, True], [True, True], [False, True], [False, False]])
+    np.testing.assert_array_equal(keep, expect)
+    # no limit, or a limit no expert reaches, keeps everything
+    assert O.kept_slots(ids, 3, 0).all() and O.kept_slots(ids, 3, 4).all()
+
+
+@pytest.mark.parametrize("T,E,k,cap", [(50, 8, 2, 7), (200, 16, 4, 30), (64, 4, 1, 1)])
+def test_kept_slots_invariants(T, E, k, cap):
+    g = rng(T + E)
+    p = 1.0 / np.arange(1, E + 1) ** 1.5
+    ids = np.stack([g.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    keep = O.kept_slots(ids, E, cap)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    kept = np.bincount(ids.ravel()[keep.ravel()], minlength=E)
+    np.testing.assert_array_equal(kept, np.minimum(counts, cap))
+    # every dropped pair comes after all kept pairs of its expert in flat order
+    flat_ids, flat_keep = ids.ravel(), keep.ravel()
+    for e in range(E):
+        pos = np.nonzero(flat_ids == e)[0]
+        assert flat_keep[pos].tolist() == [True] * min(len(pos), cap) + [False] * max(0, len(pos) - cap)
+
+
+def test_capacity_drops_are_the_tail_of_each_sorted_segment():
+    g = rng(41)
+    T, E, k, cap = 120, 6, 2, 25
+    ids = np.stack([g.choice(E, size=k, replace=False, p=[0.5, 0.2, 0.1, 0.1, 0.05, 0.05])
+                    for _ in range(T)])
+    counts, offsets, perm, inv = O.permute_with_capacity(ids, E, cap)
+    c0, o0, p0, i0 = O.permute(ids, E)
+    np.testing.assert_array_equal(counts, c0)
+    np.testing.assert_array_equal(perm, p0)
+    flat = ids.ravel()
+    for f in range(T * k):
+        e = flat[f]
+        assert (inv[f] >= 0) == (i0[f] - o0[e] < cap)
+        if inv[f] >= 0:
+            assert inv[f] == i0[f]
+    assert (inv < 0).sum() == np.maximum(counts - cap, 0).sum()
+
+
+def test_capacity_layer_equals_dense_masked_gates_and_combine():
+    E, d, I, T, k, S = 6, 12, 10, 30, 2, 1
+    ex = random_experts(E + S, d, I, 42)
+    g = rng(43)
+    x = g.standard_normal((T, d))
+    logits = g.standard_normal((T, E)) + np.array([2.0, 1.0, 0, 0, 0, 0])
+    ids, w = O.route(logits, k, True)
+    cap = O.capacity(0.75, T, k, E)
+    keep = O.kept_slots(ids, E, cap)
+    assert 0 < (~keep).sum() < keep.size
+    y = O.moe_layer(x, ex, ids, w, S, E, keep=keep)
+    # dropped slots behave as gates of zero in the all-experts reference
+    y_dense = O.moe_layer_dense(x, ex, ids, w * keep, S, E)
+    np.testing.assert_allclose(y, y_dense, rtol=1e-12, atol=1e-13)
+    # the sorted rows of the kept pairs, combined, give the same layer
+    _, _, perm, inv = O.permute_with_capacity(ids, E, cap)
+    _, rows = O.sorted_rows(x, ex, ids, perm, S, E)
+    np.testing.assert_allclose(O.combine(rows, inv, w, S), y, rtol=1e-12, atol=1e-13)
