@@ -38,7 +38,8 @@ class LayerDesc(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-                ("pre_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+                ("pre_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("capacity_factor", ctypes.c_float)]
 
 
 class ExpertWeights(ctypes.Structure):
@@ -116,9 +117,11 @@ def _check(status: int, where: str) -> None:
 
 
 def make_desc(d_model, n_experts, top_k, d_ff, n_shared=0, renormalize=False,
-              act_dtype=MOE_BF16, w_dtype=None, pre_norm=False, norm_eps=1e-5) -> LayerDesc:
+              act_dtype=MOE_BF16, w_dtype=None, pre_norm=False, norm_eps=1e-5,
+              capacity_factor=0.0) -> LayerDesc:
     return LayerDesc(d_model, n_experts, top_k, d_ff, n_shared, int(bool(renormalize)), act_dtype,
-                     act_dtype if w_dtype is None else w_dtype, int(bool(pre_norm)), norm_eps)
+                     act_dtype if w_dtype is None else w_dtype, int(bool(pre_norm)), norm_eps,
+                     capacity_factor)
 
 
 def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> ExpertWeights:

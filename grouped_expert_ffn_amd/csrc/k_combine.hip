@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int S,
   };
   for (int j = 0; j < k; ++j) {
     const int r = inv_perm[(size_t)t * k + j];
-    add(rows + (size_t)r * d + c, w[(size_t)t * k + j], true);
+    if (r >= 0) add(rows + (size_t)r * d + c, w[(size_t)t * k + j], true);  // < 0: dropped
   }
   for (int s = 0; s < S; ++s) add(rows + ((size_t)T * k + (size_t)s * T + t) * d + c, 1.f, false);
   if (residual) add(residual + (size_t)t * d + c, 1.f, false);

@@ -89,6 +89,7 @@ __device__ __forceinline__ bool map_work_t(const GemmArgs& a, Work& w) {
   w.g = tiles[2 * p];
   w.r0 = a.offsets[w.g];
   w.M = a.offsets[w.g + 1] - w.r0;
+  if (w.g < a.E && plan[3] > 0) w.M = min(w.M, plan[3]);  // capacity: the rest is dropped
   const int mt = (w.M + TBM - 1) / TBM;           // the group's M-tiles
   const int first = p - tiles[2 * p + 1] / TBM;   // the group's first tile in the list
   const int o = L - first * NT;                   // position inside the group's (N, M) block

@@ -137,7 +137,8 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   const int K = a.K, N = a.N;
   const int n0 = blockIdx.x * NB;
   const int r0 = a.offsets[g];
-  const int M = a.offsets[g + 1] - r0;
+  const int Mg = a.offsets[g + 1] - r0;
+  const int M = (g < a.E && a.plan[3] > 0) ? min(Mg, a.plan[3]) : Mg;  // capacity: the rest is dropped
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int q = lane % 8, lg = lane / 8;

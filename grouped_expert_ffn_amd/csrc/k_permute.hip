@@ -18,6 +18,10 @@
 // chunk, taking its chunk's base for each expert from the histograms of the chunks before it
 // (the same offsets the one-workgroup kernel computes, so the result is identical).
 //
+// With a capacity limit C, a row whose place in its expert's segment is C or later is
+// dropped (inv_perm = -1): the segment keeps ascending flat order, so these are the pairs
+// that reached the expert after its first C.
+//
 // The sort kernel (its first workgroup) also writes the launch plan of the grouped FFN: the
 // ascending list of groups that have rows (touched routed experts, then the shared experts)
 // and, for the MFMA path, the list of (group, first row) M-tiles.
@@ -59,9 +63,11 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
                                                   int32_t* __restrict__ perm,
                                                   int32_t* __restrict__ inv_perm,
                                                   int32_t* __restrict__ plan,
-                                                  const int32_t* __restrict__ chunk_hist) {
+                                                  const int32_t* __restrict__ chunk_hist,
+                                                  int cap) {
   __shared__ int hist[kPermWaves][256];
   __shared__ int pre[kMaxGroups];
+  __shared__ int seg[kMaxGroups];  // start of each expert's sorted segment
   __shared__ int cnt[kMaxGroups];
   __shared__ int base[kMaxGroups];
   __shared__ int touched[kMaxGroups];
@@ -173,6 +179,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
       const int e = 4 * lane + i;
       if (e < E) {
         base[e] = ex + pre[e];
+        seg[e] = ex;
         if (lead_block) {
           counts[e] = c[i];
           offsets[e] = ex;
@@ -207,7 +214,8 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
     const int pos = hist[wave][key] + __popcll(peers & lt_mask);
     if (valid) {
       perm[pos] = f;
-      inv_perm[f] = pos;
+      // with a capacity limit, rows past the first cap of the expert's segment are dropped
+      inv_perm[f] = (cap == 0 || pos - seg[key] < cap) ? pos : -1;
     }
     if (valid && lane == leader) hist[wave][key] = hist[wave][key] + __popcll(peers);
   }
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
         int rows = 0;
         if (p < n_groups) {
           const int g = touched[p];
-          rows = g < E ? cnt[g] : T;
+          rows = g < E ? (cap ? min(cnt[g], cap) : cnt[g]) : T;
         }
         nt[i] = (rows + tile_m - 1) / tile_m;
         s += nt[i];
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
     int32_t* tiles = tl + (E + S);
     for (int p = tid; p < n_groups; p += blockDim.x) {
       const int g = touched[p];
-      const int rows = g < E ? cnt[g] : T;
+      const int rows = g < E ? (cap ? min(cnt[g], cap) : cnt[g]) : T;
       int o = tile_start[p];
       for (int m0 = 0; m0 < rows; m0 += tile_m, ++o) {
         tiles[2 * o] = g;
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
   if (tid == 0) {
     plan[0] = n_groups;
     plan[2] = tile_m;
-    plan[3] = 0;
+    plan[3] = cap;
   }
 }
 
@@ -301,7 +309,7 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
   if (N <= kSingleMaxRows) {
     k_permute<false><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
-                                        offsets, perm, inv_perm, plan, nullptr);
+                                        offsets, perm, inv_perm, plan, nullptr, capacity_rows(L, T));
     return hipGetLastError();
   }
   // the timer brackets both launches: it records its start before the first and its stop
@@ -310,7 +318,8 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
   const int nb = (N + kPermChunk - 1) / kPermChunk;
   k_perm_hist<<<nb, 1024, 0, s>>>(N, L.E, ids, chunk_hist);
   k_permute<false><<<nb, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
-                                       offsets, perm, inv_perm, plan, chunk_hist);
+                                       offsets, perm, inv_perm, plan, chunk_hist,
+                                       capacity_rows(L, T));
   return hipGetLastError();
 }
 
@@ -321,7 +330,8 @@ hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, i
                                int32_t* inv_perm, int32_t* plan, int tile_m, hipStream_t s) {
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
   k_permute<true><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, logits, L.renorm, topk_w, ids,
-                                     counts, offsets, perm, inv_perm, plan, nullptr);
+                                     counts, offsets, perm, inv_perm, plan, nullptr,
+                                     capacity_rows(L, T));
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ int32_t check_desc(const moe_layer_desc_t* d, LayerDims* L) {
   if (d->pre_norm != 0 && d->pre_norm != 1) return fail(MOE_ERR_INVALID, "pre_norm must be 0 or 1");
   if (d->pre_norm && !(d->norm_eps >= 0.f && d->norm_eps < 1e30f))
     return fail(MOE_ERR_INVALID, "norm_eps must be finite and >= 0");
+  if (!(d->capacity_factor >= 0.f && d->capacity_factor < 1e30f))
+    return fail(MOE_ERR_INVALID, "capacity_factor must be finite and >= 0");
   if (d->n_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 256");
   if (d->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
   if (d->n_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "n_shared > 8");
@@ -67,7 +69,7 @@ int32_t check_desc(const moe_layer_desc_t* d, LayerDims* L) {
     return fail(MOE_ERR_UNSUPPORTED, "dtype combination act=%d w=%d (supported: f32/f32, bf16/bf16, bf16/i8)",
                 d->act_dtype, d->w_dtype);
   *L = LayerDims{d->d_model, d->n_experts, d->top_k, d->d_ff, d->n_shared, d->renormalize,
-                 d->act_dtype, d->w_dtype};
+                 d->act_dtype, d->w_dtype, d->capacity_factor};
   return MOE_OK;
 }
 

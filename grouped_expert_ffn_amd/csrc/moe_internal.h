@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "moe.h"
 
 namespace moe {
@@ -123,7 +125,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 //   [0] number of groups with rows (touched routed experts + shared experts)
 //   [1] number of M-tiles in the tile list
 //   [2] M-tile height the tile list was built for
-//   [3] reserved
+//   [3] capacity C: routed group g holds min(rows, C) rows (0 = no limit)
 //   [4 .. 4+E+S)            touched group ids, ascending (routed first, then shared)
 //   [4+E+S .. + 2*max_tiles) tile list: (group, first row within the group)
 //   then, for the multi-workgroup sort, one expert histogram per chunk of kPermChunk rows
@@ -157,7 +159,17 @@ class LaunchTimer {
 
 struct LayerDims {
   int d, E, k, I, S, renorm, act, wdt;
+  float cf;  // capacity factor, 0 = dropless
 };
+
+// Rows each routed expert keeps: ceil(cf * T * k / E) formed in double in that order, 0 for
+// no limit.  An expert never holds more than T rows (a token picks it at most once), so the
+// value is capped at T, which changes nothing.
+inline int capacity_rows(const LayerDims& L, int T) {
+  if (!(L.cf > 0.f)) return 0;
+  const double c = std::ceil((double)L.cf * T * L.k / L.E);
+  return c >= (double)T ? T : (int)c;
+}
 
 hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, float eps,
                           hipStream_t s);

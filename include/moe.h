@@ -76,6 +76,10 @@ typedef struct {
                           act_dtype BF16 (int8 weight-only)                                */
   int32_t pre_norm;    /* moe_forward only: 1 = RMSNorm(x) (no scale) before the layer    */
   float norm_eps;      /* epsilon of that RMSNorm                                          */
+  float capacity_factor; /* 0: dropless.  > 0: each routed expert keeps its first
+                          C = ceil(capacity_factor * T * k / E) rows (switchyard §03 "Load
+                          balance": a capacity limit drops what an expert has no room for);
+                          see moe_permute                                                  */
 } moe_layer_desc_t;
 
 typedef struct {
@@ -117,9 +121,13 @@ int32_t moe_route(const moe_layer_desc_t* desc, int32_t T, const void* x, const 
  *   offsets[g]  start of group g's rows; offsets[E] = T*k; shared expert s owns rows
  *               T*k + s*T .. T*k + (s+1)*T - 1 in token order           [E+S+1]  int32
  *   perm[r]     flat index f of sorted row r; rows of one expert keep ascending f
- *   inv_perm[f] sorted position of flat row f                           [T*k]    int32
+ *   inv_perm[f] sorted position of flat row f, or -1 if the row was dropped  [T*k] int32
  *   plan        device buffer of plan_bytes >= moe_workspace_bytes(desc, T, MOE_WS_PERMUTE);
  *               receives the touched-expert list and tile list that moe_grouped_ffn reads.
+ * With desc->capacity_factor > 0, expert e keeps the first C of its rows (the lowest flat
+ * indices, i.e. the head of its sorted segment) and the others are dropped: their inv_perm
+ * is -1, moe_grouped_ffn leaves them unwritten and moe_combine skips them.  counts,
+ * offsets and perm still describe every row.  Shared experts never drop.
  * topk_ids must hold values in [0, E); other values give unspecified (but in-bounds)
  * results. */
 int32_t moe_permute(const moe_layer_desc_t* desc, int32_t T, const int32_t* topk_ids,
@@ -134,8 +142,8 @@ int32_t moe_permute(const moe_layer_desc_t* desc, int32_t T, const int32_t* topk
  * with int8 weights: W[g][n,:] = q[g][n,:] * s[g][n] (per output channel), the scale being
  * applied to the fp32 accumulator.  Accumulation is fp32; h is rounded to act_dtype.
  * x [T,d]; offsets, perm as written by moe_permute; plan as written by that same
- * moe_permute call; rows [T*k + S*T, d] act_dtype (output); ws >= moe_workspace_bytes(
- * desc, T, MOE_WS_GROUPED_FFN). */
+ * moe_permute call; rows [T*k + S*T, d] act_dtype (output: the rows of dropped slots are
+ * left unwritten); ws >= moe_workspace_bytes(desc, T, MOE_WS_GROUPED_FFN). */
 int32_t moe_grouped_ffn(const moe_layer_desc_t* desc, int32_t T, const void* x,
                         const moe_expert_weights_t* weights, const int32_t* offsets,
                         const int32_t* perm, const void* plan, void* rows, void* ws,
@@ -146,8 +154,9 @@ int32_t moe_grouped_ffn(const moe_layer_desc_t* desc, int32_t T, const void* x,
  *   y[t] = sum_{j<k} topk_w[t,j] * rows[inv_perm[t*k+j]] + sum_{s<S} rows[T*k+s*T+t]
  *          + residual[t]
  * summed in fp32 in exactly that order, rounded once to act_dtype.
- * rows [T*k+S*T, d]; inv_perm [T*k]; topk_w [T,k] fp32; residual [T,d] or NULL (may be
- * the same buffer as y); y [T,d] act_dtype. */
+ * rows [T*k+S*T, d]; inv_perm [T*k] (a slot with inv_perm < 0 was dropped by the
+ * capacity limit and adds nothing); topk_w [T,k] fp32; residual [T,d] or NULL (may be the
+ * same buffer as y); y [T,d] act_dtype. */
 int32_t moe_combine(const moe_layer_desc_t* desc, int32_t T, const void* rows,
                     const int32_t* inv_perm, const float* topk_w, const void* residual,
                     void* y, void* stream);

@@ -78,6 +78,9 @@ def test_workspace_sizes(L):
     (dict(n_experts=0), abi.MOE_ERR_INVALID),
     (dict(d_model=-8), abi.MOE_ERR_INVALID),
     (dict(n_shared=-1), abi.MOE_ERR_INVALID),
+    (dict(capacity_factor=-1.0), abi.MOE_ERR_INVALID),
+    (dict(capacity_factor=float("nan")), abi.MOE_ERR_INVALID),
+    (dict(capacity_factor=float("inf")), abi.MOE_ERR_INVALID),
     (dict(n_experts=512), abi.MOE_ERR_UNSUPPORTED),
     (dict(top_k=17, n_experts=64), abi.MOE_ERR_UNSUPPORTED),
     (dict(d_model=2040), abi.MOE_ERR_UNSUPPORTED),

@@ -332,3 +332,72 @@ def test_stack_staged_per_layer():
     print(f"stack: busiest/mean per layer {[round(s, 2) for s in skews]}, tie flips {flips}")
     # the tuned skew holds on layer 0 (later layers drift)
     assert 3.9 <= skews[0] <= 4.1, skews
+
+
+# ----------------------------------------------------------------------------------------
+# option: capacity-factor dropping
+# ----------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k,S_", [(16, 8, 2, 0), (300, 8, 2, 1), (1000, 64, 6, 2),
+                                      (2048, 64, 8, 0), (2100, 64, 6, 2)])
+@pytest.mark.parametrize("cf", [0.5, 1.0, 2.0])
+def test_permute_with_capacity_is_bit_exact(T, E, k, S_, cf):
+    from grouped_expert_ffn_amd import (MOE_WS_PERMUTE, alloc_workspace, make_desc, moe_permute,
+                                        moe_workspace_bytes, to_device)
+    t = T_()
+    ids = ids_case("zipf", T, E, k, seed=T + E + k + 7)
+    desc = make_desc(64, E, k, 64, n_shared=S_, capacity_factor=cf)
+    counts = t.full((E,), -7, dtype=t.int32, device="cuda")
+    offsets = t.full((E + S_ + 1,), -7, dtype=t.int32, device="cuda")
+    perm = t.full((T * k,), -7, dtype=t.int32, device="cuda")
+    inv = t.full((T * k,), -7, dtype=t.int32, device="cuda")
+    pb = moe_workspace_bytes(desc, T, MOE_WS_PERMUTE)
+    plan = alloc_workspace(pb)
+    moe_permute(desc, T, to_device(ids), counts, offsets, perm, inv, plan, pb)
+    t.cuda.synchronize()
+    cap = O.capacity(cf, T, k, E)
+    c_ref, o_ref, p_ref, i_ref = O.permute_with_capacity(ids, E, cap)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(offsets.cpu().numpy()[:E + 1], o_ref)
+    np.testing.assert_array_equal(perm.cpu().numpy(), p_ref)
+    np.testing.assert_array_equal(inv.cpu().numpy(), i_ref)
+    assert (i_ref < 0).any() or cf == 2.0
+    pl = plan.view(t.int32).cpu().numpy()
+    assert pl[3] == min(cap, T)
+    tm = pl[2]
+    if tm > 0:
+        touched = [e for e in range(E) if c_ref[e] > 0] + [E + s for s in range(S_)]
+        rows = {g: (min(c_ref[g], cap) if g < E else T) for g in touched}
+        tiles = pl[4 + E + S_: 4 + E + S_ + 2 * pl[1]].reshape(-1, 2)
+        assert [tuple(x) for x in tiles.tolist()] == [(g, m0) for g in touched
+                                                      for m0 in range(0, rows[g], tm)]
+
+
+CAP_CASES = [(SMALL_ZIPF, 300, 1.0), (SMALL_RING, 300, 1.0), (SMALL_RING, 40, 0.5),
+             (S.OLMOE_BF16, 8, 1.0), (S.OLMOE_I8_ZIPF, 8, 1.0), (S.DEEPSEEK_BF16, 2048, 1.0),
+             (S.DEEPSEEK_BF16, 16, 2.0)]
+
+
+@pytest.mark.parametrize("wl,T,cf", CAP_CASES, ids=case_id)
+def test_forward_with_capacity(wl, T, cf):
+    from grouped_expert_ffn_amd import DeviceLayer, make_desc, to_device, DTYPES
+    t = T_()
+    gl = C.GpuLayer(wl)
+    desc = make_desc(wl.d, wl.E, wl.k, wl.I, wl.S, wl.renormalize, DTYPES[wl.act], DTYPES[wl.wdt],
+                     capacity_factor=cf)
+    dl = DeviceLayer(desc, gl.dev.w_router, gl.dev.bias, gl.dev.w_gate, gl.dev.w_up, gl.dev.w_down,
+                     gl.dev.s_gate, gl.dev.s_up, gl.dev.s_down)
+    x = S.make_tokens(wl, T)
+    ids = t.empty((T, wl.k), dtype=t.int32, device="cuda")
+    y = dl.forward(to_device(x), topk_ids=ids)
+    t.cuda.synchronize()
+    ids_g = ids.cpu().numpy()
+    cap = O.capacity(cf, T, wl.k, wl.E)
+    keep = O.kept_slots(ids_g, wl.E, cap)
+    if cf <= 1.0:
+        assert (~keep).any(), "the case is meant to drop rows"
+    logits = O.router_logits(x, gl.host.w_router, gl.host.bias)
+    C.check_routing_against_oracle(ids_g, logits, wl.k)
+    w_ref = O.gate_weights_for(logits, ids_g, wl.renormalize)
+    tok = list(range(T)) if T <= 300 else sorted(set(range(0, T, 97)) | {T - 1})
+    y_ref = O.moe_layer(x, gl.experts, ids_g, w_ref, wl.S, wl.E, tokens=tok, keep=keep)
+    C.assert_close(C.widen_dev(y)[tok], y_ref, wl.act, f"{wl.name} T={T} cf={cf}")
