@@ -6,8 +6,11 @@ grouped down, combine) over one batch of seeded synthetic tokens whose weights
 and inputs are already resident in HBM.  The headline workload is the
 OLMoE-shaped decode layer (d=2048, E=64, k=8, I=1024, bf16) at T=8 tokens.
 
-Before anything is timed, the layer's output on sampled tokens is checked
-against the fp64 CPU oracle; a disagreeing build is refused, not timed.
+Before a point is timed its output must be finite and bit-identical over two
+runs.  Agreement with the fp64 CPU oracle is what the GPU test suite checks;
+here the CPU-baseline leg, which runs the oracle on a sample of the headline
+tokens anyway, also compares its outputs with the GPU's for those tokens and
+withholds the JSON line if they disagree.
 
 The expert weights are replicated ``--copies`` times and the steps rotate over
 the copies, so the 256 MiB Infinity Cache cannot serve the weights of the next
@@ -59,6 +62,9 @@ def parse():
                    help="extra workload:T points timed after the headline ('' for none)")
     p.add_argument("--sweep-steps", type=int, default=20)
     p.add_argument("--no-stack", action="store_true", help="skip the 16-layer prefill stack")
+    p.add_argument("--capacity", default="deepseek_bf16:2048@1.0,deepseek_bf16:2048@2.0,"
+                   "olmoe_stack16:2048@1.0,olmoe_stack16:2048@2.0",
+                   help="workload:T@capacity_factor points with token dropping ('' for none)")
     p.add_argument("--stack-steps", type=int, default=5, help="timed passes over the 16 layers")
     p.add_argument("--no-extras", action="store_true",
                    help="skip graph replay, copies plateau and copy ceiling")
@@ -278,9 +284,10 @@ def _call(lib, args):
 
 
 class Point:
-    """One layer at T tokens, its weights replicated `copies` times on the GPU."""
+    """One layer at T tokens, its weights replicated `copies` times on the GPU (layer 0 of the
+    workload; `cf` > 0 turns on capacity-factor dropping)."""
 
-    def __init__(self, wl, T, copies, seed=0):
+    def __init__(self, wl, T, copies, seed=0, cf=0.0):
         import torch
 
         import moe_synth as S
@@ -288,8 +295,9 @@ class Point:
         self.wl, self.T = wl, T
         self.host = host_layer(wl, seed)
         self.x_host = S.make_tokens(wl, T, seed)
+        self.cf = cf
         self.desc = make_desc(wl.d, wl.E, wl.k, wl.I, wl.S, wl.renormalize, DTYPES[wl.act],
-                              DTYPES[wl.wdt], wl.pre_norm, wl.norm_eps)
+                              DTYPES[wl.wdt], wl.pre_norm, wl.norm_eps, cf)
         h = self.host
         base = DeviceLayer(self.desc, h.w_router, h.bias, h.w_gate, h.w_up, h.w_down, h.s_gate,
                            h.s_up, h.s_down)
@@ -319,21 +327,22 @@ class Point:
         torch.cuda.synchronize()
         return self.ids.cpu().numpy()
 
-    def parity_gate(self, n_tokens=8):
-        """Check sampled tokens against the fp64 oracle; raise if they disagree."""
-        import numpy as np
+    def sanity_gate(self):
+        """Refuse to time a layer whose output is not finite or not bit-identical over two
+        runs; keeps the output and routing of the checked run."""
+        import torch
 
         from grouped_expert_ffn_amd import from_device
-        from oracle import moe_oracle as O
         ids = self.routing()
-        y = O.widen(from_device(self.y))
-        T = self.T
-        tok = sorted(set(np.linspace(0, T - 1, min(T, n_tokens)).astype(int).tolist()))
-        logits = O.router_logits(self.x_host[tok], self.host.w_router, self.host.bias)
-        w = O.gate_weights_for(logits, ids[tok], self.wl.renormalize)
-        ref = O.moe_layer(self.x_host[tok], O.Experts.from_layer(self.host), ids[tok], w,
-                          self.wl.S, self.wl.E)
-        return _gate(self.wl, f"T={T}", y[tok], ref)
+        y1 = from_device(self.y).copy()
+        ids2 = self.routing()
+        y2 = from_device(self.y)
+        yf = self.y.float()
+        if not (bool(torch.isfinite(yf).all()) and (y1 == y2).all() and (ids == ids2).all()):
+            raise SystemExit(f"{self.wl.name} T={self.T}: output not finite or not deterministic; "
+                             "refusing to time")
+        self.y_host, self.ids_host = y1, ids
+        return ids
 
     def graph_ms(self, replays):
         """One graph holds one forward per weight copy; ms per layer of a replay."""
@@ -353,17 +362,6 @@ class Point:
         self.layers.clear()
         self.args.clear()
         torch.cuda.empty_cache()
-
-
-def _gate(wl, what, got, ref):
-    import numpy as np
-    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
-    lim = 1e-5 if wl.act == "f32" else 1e-2
-    if not (rel <= lim and mx <= 2e-2):
-        raise SystemExit(f"parity gate FAILED for {wl.name} {what}: rel-L2 {rel:.3e}, "
-                         f"max-abs/max {mx:.3e}; refusing to time")
-    return rel
 
 
 def roofline_for(wl, T, work, kern_ms, traffic=None):
@@ -394,8 +392,7 @@ def measure(wl, T, steps, warmup, copies, extras=False):
 
     from grouped_expert_ffn_amd import abi
     pt = Point(wl, T, copies)
-    rel = pt.parity_gate()
-    ids = pt.routing()
+    ids = pt.sanity_gate()
     n_touched = int(np.count_nonzero(np.bincount(ids.ravel(), minlength=wl.E)))
     work = layer_work(wl, T, n_touched)
     ms, wall = time_steps(pt.step, steps, warmup)
@@ -410,7 +407,7 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         "gate_up_ms": round(gu_ms, 5), "down_ms": round(dn_ms, 5),
         "gate_up_hbm_frac": round(work["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "down_hbm_frac": round(work["down_bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "touched_experts": n_touched, "parity_rel_l2": float(f"{rel:.3e}"),
+        "touched_experts": n_touched,
     }
     if T > 8 and wl.act == "bf16":
         res["gate_up_mfma_frac"] = round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
@@ -419,8 +416,9 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         res["step_ms_percentiles"] = step_percentiles(pt.step, steps)
         res["graph_ms_per_layer"] = round(pt.graph_ms(max(4, steps // copies)), 5)
     roof = roofline_for(wl, T, work, gu_ms)
+    checked = (pt.x_host, pt.y_host, pt.ids_host)
     pt.free()
-    return res, roof, ms, wall, work
+    return res, roof, ms, wall, work, checked
 
 
 def copies_plateau(wl, T, counts=(1, 2, 4, 8, 16), steps=32):
@@ -450,11 +448,8 @@ class Stack:
                               DTYPES[wl.wdt], wl.pre_norm, wl.norm_eps)
         self.x_host = S.make_tokens(wl, T)
         self.layers = []
-        self.host0 = None
         for layer in range(wl.n_layers):
             h = S.make_layer(wl, layer)
-            if layer == 0:
-                self.host0 = h
             self.layers.append(DeviceLayer(self.desc, h.w_router, h.bias, h.w_gate, h.w_up, h.w_down))
             del h
         self.x0 = to_device(self.x_host)
@@ -475,39 +470,34 @@ class Stack:
     def layer(self, i):
         _call(self.lib, self.args[i % len(self.args)])
 
-    def parity_gate(self, n_tokens=8):
-        """Layer 0 on sampled tokens against the oracle fed the same bf16 input."""
+    def sanity_gate(self):
+        """Layer 0 twice: the output must be finite and bit-identical; records the busiest
+        expert's load over the mean."""
         import numpy as np
         import torch
 
-        from grouped_expert_ffn_amd import from_device
-        from oracle import moe_oracle as O
         wl, T = self.wl, self.T
-        self.layers[0].forward(self.x0, residual=self.x0, y=self.buf[0], topk_ids=self.ids)
-        torch.cuda.synchronize()
-        ids = self.ids.cpu().numpy()
-        tok = sorted(set(np.linspace(0, T - 1, n_tokens).astype(int).tolist()))
-        xn = O.stack_layer_input(self.x_host[tok], wl.norm_eps)
-        logits = O.router_logits(xn, self.host0.w_router, self.host0.bias)
-        w = O.gate_weights_for(logits, ids[tok], wl.renormalize)
-        ref = O.moe_layer(xn, O.Experts.from_layer(self.host0), ids[tok], w, 0, wl.E,
-                          residual=self.x_host[tok])
-        counts = np.bincount(ids.ravel(), minlength=wl.E)
+        outs = []
+        for _ in range(2):
+            self.layers[0].forward(self.x0, residual=self.x0, y=self.buf[0], topk_ids=self.ids)
+            torch.cuda.synchronize()
+            outs.append(self.buf[0].clone())
+        if not (bool(torch.isfinite(outs[0].float()).all()) and torch.equal(outs[0], outs[1])):
+            raise SystemExit("stack layer 0: output not finite or not deterministic; refusing to time")
+        counts = np.bincount(self.ids.cpu().numpy().ravel(), minlength=wl.E)
         self.skew0 = float(counts.max() / (T * wl.k / wl.E))
-        return _gate(wl, f"stack layer 0 T={T}", O.widen(from_device(self.buf[0]))[tok], ref)
 
     def free(self):
         import torch
         self.layers.clear()
         self.args.clear()
-        self.host0 = None
         torch.cuda.empty_cache()
 
 
 def measure_stack(wl, steps):
     from grouped_expert_ffn_amd import abi
     st = Stack(wl, wl.tokens[0])
-    rel = st.parity_gate()
+    st.sanity_gate()
     T, n = st.T, wl.n_layers
     ms, _ = time_steps(st.step, steps, 2)
     gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, st.layer, 2 * n)
@@ -522,34 +512,73 @@ def measure_stack(wl, steps):
         "gate_up_ms": round(gu_ms, 5), "down_ms": round(dn_ms, 5),
         "gate_up_mfma_frac": round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "down_mfma_frac": round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
-        "busiest_over_mean_layer0": round(st.skew0, 3), "parity_rel_l2_layer0": float(f"{rel:.3e}"),
+        "busiest_over_mean_layer0": round(st.skew0, 3),
     }
     st.free()
     return res
 
 
+def drop_stats(ids, E, cf):
+    """Rows per routed expert C = ceil(cf*T*k/E) (the library's rule) and which (token, slot)
+    pairs fall past the first C of their expert, the pairs reaching experts in flat order."""
+    import numpy as np
+    T, k = ids.shape
+    cap = int(np.ceil(float(np.float32(cf)) * T * k / E)) if cf > 0 else 0
+    flat = ids.ravel()
+    order = np.argsort(flat, kind="stable")
+    starts = np.searchsorted(flat[order], np.arange(E))
+    rank = np.empty(flat.size, dtype=np.int64)
+    rank[order] = np.arange(flat.size) - starts[flat[order]]
+    dropped = (rank >= cap).reshape(T, k) if cap > 0 else np.zeros((T, k), dtype=bool)
+    return cap, dropped
+
+
+def measure_capacity(wl, T, cf, steps, copies):
+    """Layer time with capacity-factor dropping, and how much is dropped (the GPU's own
+    routing)."""
+    import numpy as np
+    pt = Point(wl, T, copies, cf=cf)
+    ids = pt.sanity_gate()
+    cap, dropped = drop_stats(ids, wl.E, cf)
+    ms, _ = time_steps(pt.step, steps, 3)
+    pt.free()
+    counts = np.bincount(ids.ravel(), minlength=wl.E)
+    return {"workload": wl.name, "tokens": T, "capacity_factor": cf, "capacity_rows": cap,
+            "ms_per_layer": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "dropped_pairs_frac": round(float(dropped.mean()), 4),
+            "tokens_with_a_drop_frac": round(float(dropped.any(axis=1).mean()), 4),
+            "busiest_over_mean": round(float(counts.max() / (T * wl.k / wl.E)), 3)}
+
+
 # ------------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands
 # ------------------------------------------------------------------------------------------
-def cpu_baseline(wl, T, budget_s):
-    """The fp64 oracle as it stands, on a bounded sample of the same workload."""
-    import moe_synth as S
+def cpu_baseline(wl, T, budget_s, checked):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload.  The outputs it
+    produces for the headline tokens are also compared with the GPU's (`checked`: tokens,
+    output bits and routing of the run the sanity gate kept), wherever the oracle picked the
+    same experts; a disagreement withholds the bench line."""
+    import numpy as np
+
     from oracle import moe_oracle as O
     host = host_layer(wl)
-    x = S.make_tokens(wl, T)
+    x_host, y_gpu, ids_gpu = checked
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = 1
     done, passes = 0, 0
+    first_pass = []  # (token, oracle ids, oracle output) of the first pass, compared afterwards
     t0 = time.perf_counter()
     while True:
         ex = O.Experts.from_layer(host)  # every pass widens the stored weights again
         for t in range(T):
-            xt = x[t:t + 1]
+            xt = x_host[t:t + 1]
             logits, ids, w = O.full_route(xt, host.w_router, host.bias, wl.k, wl.renormalize)
-            O.moe_layer(xt, ex, ids, w, wl.S, wl.E)
+            y = O.moe_layer(xt, ex, ids, w, wl.S, wl.E)
+            if passes == 0:
+                first_pass.append((t, ids[0], y[0]))
             done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -557,9 +586,22 @@ def cpu_baseline(wl, T, budget_s):
         if time.perf_counter() - t0 > budget_s * 0.66 or done >= 64 * T:
             break
     el = time.perf_counter() - t0
-    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} tokens of {wl.name} T={T} ({passes} pass(es), fp64 per-token "
-                      f"per-expert loop incl. weight widening), {el:.1f} s"}
+    out = {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{done} tokens of {wl.name} T={T} ({passes} pass(es), fp64 per-token "
+                     f"per-expert loop incl. weight widening), {el:.1f} s"}
+    same = [(t, y) for t, ids, y in first_pass if np.array_equal(ids, ids_gpu[t])]
+    if same:
+        ref = np.array([y for _, y in same])
+        got = O.widen(y_gpu[[t for t, _ in same]])
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        out["parity"] = {"tokens": len(first_pass), "same_routing": len(same),
+                         "rel_l2": float(f"{rel:.3e}"), "max_abs_over_max": float(f"{mx:.3e}")}
+        lim = 1e-5 if wl.act == "f32" else 1e-2
+        if not (rel <= lim and mx <= 2e-2):
+            raise SystemExit(f"oracle disagrees with the GPU on {wl.name} T={T}: rel-L2 {rel:.3e}, "
+                             f"max-abs/max {mx:.3e}; no bench line")
+    return out
 
 
 def counters_pass(wl, T, steps, warmup, copies):
@@ -573,7 +615,7 @@ def counters_pass(wl, T, steps, warmup, copies):
     torch.cuda.synchronize()
     del a, b
     pt = Point(wl, T, copies)
-    pt.parity_gate()
+    pt.sanity_gate()
     time_steps(pt.step, steps, warmup)
     pt.free()
     print(f"counters pass done: {wl.name} T={T}, {steps} steps", flush=True)
@@ -594,8 +636,8 @@ def main():
     if args.counters_pass:
         counters_pass(wl, args.tokens, args.steps, args.warmup, args.copies)
         return
-    res, roof, ms, wall, work = measure(wl, args.tokens, args.steps, args.warmup, args.copies,
-                                        extras=not args.no_extras)
+    res, roof, ms, wall, work, checked = measure(wl, args.tokens, args.steps, args.warmup, args.copies,
+                                                 extras=not args.no_extras)
     kind = "gemm" if "GEMM" in roof["kernel"] else "gemv"
     roof["traffic"] = read_traffic(f"{kind}_gateup_{wl.name}_T{args.tokens}.pmc.txt")
     print(f"# headline {wl.name} T={args.tokens}: {ms:.4f} ms/layer", file=sys.stderr, flush=True)
@@ -619,7 +661,15 @@ def main():
         stack = measure_stack(S.OLMOE_STACK16, args.stack_steps)
         print(f"# stack: {stack['ms_per_stack']:.3f} ms / {stack['layers']} layers", file=sys.stderr,
               flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.tokens, args.cpu_seconds)
+    capacity = []
+    for item in [c for c in args.capacity.split(",") if c.strip()]:
+        point, cf = item.split("@")
+        name, t = point.split(":")
+        r = measure_capacity(S.WORKLOADS[name], int(t), float(cf), args.sweep_steps, args.copies)
+        capacity.append(r)
+        print(f"# capacity {name} T={t} cf={cf}: {r['ms_per_layer']:.4f} ms/layer, "
+              f"{100 * r['dropped_pairs_frac']:.1f}% of pairs dropped", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.tokens, args.cpu_seconds, checked)
     out = {
         "metric": "MoE-layer tokens/s (one MoE layer forward, T tokens per step)",
         "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -636,6 +686,7 @@ def main():
         "extras": extras,
         "sweep": sweep,
         "stack": stack,
+        "capacity": capacity,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
