@@ -45,7 +45,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 
-DEFAULT_SWEEP = ("olmoe_bf16:1,olmoe_bf16:64,olmoe_i8:1,olmoe_i8:8,olmoe_i8:64,olmoe_i8_zipf:8,"
+DEFAULT_SWEEP = ("olmoe_bf16:1,olmoe_bf16:2,olmoe_bf16:4,olmoe_bf16:9,olmoe_bf16:64,"
+                 "olmoe_i8:1,olmoe_i8:8,olmoe_i8:64,olmoe_i8_zipf:8,"
                  "deepseek_bf16:1,deepseek_bf16:16,deepseek_bf16:128,deepseek_bf16:512,"
                  "deepseek_bf16:2048")
 
@@ -59,12 +60,12 @@ def parse():
     p.add_argument("--tokens", type=int, default=8)
     p.add_argument("--copies", type=int, default=8, help="weight replicas rotated over (cache defeat)")
     p.add_argument("--sweep", default=DEFAULT_SWEEP,
-                   help="extra workload:T points timed after the headline ('' for none)")
+                   help="extra workload:T points timed after the headline ('' or none for none)")
     p.add_argument("--sweep-steps", type=int, default=20)
     p.add_argument("--no-stack", action="store_true", help="skip the 16-layer prefill stack")
     p.add_argument("--capacity", default="deepseek_bf16:2048@1.0,deepseek_bf16:2048@2.0,"
                    "olmoe_stack16:2048@1.0,olmoe_stack16:2048@2.0",
-                   help="workload:T@capacity_factor points with token dropping ('' for none)")
+                   help="workload:T@capacity_factor points with token dropping ('' or none for none)")
     p.add_argument("--stack-steps", type=int, default=5, help="timed passes over the 16 layers")
     p.add_argument("--no-extras", action="store_true",
                    help="skip graph replay, copies plateau and copy ceiling")
@@ -646,7 +647,7 @@ def main():
         extras["copies_plateau_ms"] = copies_plateau(wl, args.tokens)
         extras["copy_ceiling_gbs"] = copy_ceiling_gbs()
     sweep = []
-    for item in [s for s in args.sweep.split(",") if s.strip()]:
+    for item in [s for s in args.sweep.split(",") if s.strip() and s.strip() != "none"]:
         name, t = item.split(":")
         if name == wl.name and int(t) == args.tokens:
             continue
@@ -662,7 +663,7 @@ def main():
         print(f"# stack: {stack['ms_per_stack']:.3f} ms / {stack['layers']} layers", file=sys.stderr,
               flush=True)
     capacity = []
-    for item in [c for c in args.capacity.split(",") if c.strip()]:
+    for item in [c for c in args.capacity.split(",") if c.strip() and c.strip() != "none"]:
         point, cf = item.split("@")
         name, t = point.split(":")
         r = measure_capacity(S.WORKLOADS[name], int(t), float(cf), args.sweep_steps, args.copies)

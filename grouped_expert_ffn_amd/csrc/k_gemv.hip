@@ -272,16 +272,18 @@ hipError_t run_gemv(const GemvArgs& a, int slots, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Pick MAXIT (K steps per wavefront) so one round covers K when possible, and CPG so a
-// lane issues about 16 weight loads per N-block.
+// Pick MAXIT (K steps per wavefront) so one round covers K when possible, and CPG (channel
+// groups per block).  Measured on the OLMoE shapes: more, smaller blocks beat fewer blocks
+// with more loads per lane once a block's loads fill a round trip, so the down projection
+// uses 2 channel groups and int8 gate/up 1 (a lane's 16 bytes hold twice the weights).
 template <int MODE, typename AT, typename WT>
 hipError_t dispatch_gemv(const GemvArgs& a, int slots, hipStream_t s) {
   constexpr int V = WTraits<WT>::V;
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   const int steps = (a.K + 8 * V - 1) / (8 * V);
   const int spw = (steps + kWaves - 1) / kWaves;
-  if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 8), 2>(a, slots, s);
-  if (spw <= 4) return run_gemv<MODE, AT, WT, 2, 4>(a, slots, s);
+  if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 2), 2>(a, slots, s);
+  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 2 && V == 16 ? 1 : 2), 4>(a, slots, s);
   return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8>(a, slots, s);
 }
 

@@ -171,6 +171,9 @@ FULL_CASES = [  # every row checked
     (S.TINY_F32, 16), (SMALL_RAGGED, 100), (SMALL_RAGGED, 7), (SMALL_RAGGED_I8, 100),
     (SMALL_RAGGED_I8, 5), (SMALL_ZIPF, 300), (SMALL_RING, 300), (SMALL_RING, 40),
     (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8),
+    # speculative-decode verify batches (draft length + 1 tokens): T = 3 on the GEMV,
+    # T = 9 the first size on the matrix-core GEMM
+    (S.OLMOE_BF16, 3), (S.OLMOE_BF16, 9),
     (S.OLMOE_I8, 1), (S.OLMOE_I8, 8), (S.DEEPSEEK_BF16, 1), (S.OLMOE_I8_ZIPF, 8),
 ]
 SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
