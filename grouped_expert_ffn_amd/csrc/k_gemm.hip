@@ -317,28 +317,56 @@ typedef const __attribute__((address_space(1))) void global_void;
 constexpr int RBM = 128, RBN = 256, RWN = 4;
 constexpr int R_THREADS = 64 * RWN;
 constexpr int R_TI = RBM / 16, R_TJ = RBN / RWN / 16;  // 16x16 MFMA tiles per wavefront
-constexpr int R_A_BYTES = RBM * RBK * 2, R_STAGE = (RBM + RBN) * RBK * 2;
-constexpr int R_DMA_A = RBM / 16 / RWN, R_DMA_B = RBN / 16 / RWN;  // loads per stage per wave
-constexpr int R_LPS = R_DMA_A + R_DMA_B;
-constexpr size_t R_LDS = (size_t)RNST * R_STAGE;
-static_assert((RNST - 2) * R_LPS < 16, "vmcnt range");
+constexpr int R_A_BYTES = RBM * RBK * 2;
+constexpr int R_DMA_A = RBM / 16 / RWN;  // A loads per stage per wavefront
 
-template <int MODE>
+// Stage geometry for bf16 (W8 = false) or int8 (W8 = true) weights: B rows of RBK weights.
+template <bool W8>
+struct RingB {
+  static constexpr int ROW = RBK * (W8 ? 1 : 2);          // bytes per B row per stage
+  static constexpr int BYTES = RBN * ROW;
+  static constexpr int STAGE = R_A_BYTES + BYTES;
+  static constexpr int LPR = ROW / 16;                     // DMA lanes per B row
+  static constexpr int RPI = 64 / LPR;                     // B rows per DMA load
+  static constexpr int DMA = RBN / RPI / RWN;              // B loads per stage per wavefront
+  static constexpr int LPS = R_DMA_A + DMA;                // loads per stage per wavefront
+  static constexpr size_t LDS = (size_t)RNST * STAGE;
+  static_assert((RNST - 2) * LPS < 16, "vmcnt range");
+};
+
+// 8 int8 weights -> 8 bf16 (exact for |q| <= 127)
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(const uint2& q) {
+  uint32_t o[4];
+  const uint32_t w[2] = {q.x, q.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int32_t v = (int32_t)w[i];
+    o[2 * i] = pack_bf16x2((float)((v << 24) >> 24), (float)((v << 16) >> 24));
+    o[2 * i + 1] = pack_bf16x2((float)((v << 8) >> 24), (float)(v >> 24));
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+template <int MODE, bool W8>
 __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_ring(
     const GemmArgs a) {
+  using B = RingB<W8>;
   extern __shared__ __align__(16) unsigned char rlds[];
   Work w;
   if (!map_work_t<RBM>(a, w)) return;
   const int K = a.K;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
-  // DMA assignment: a stage holds RBM A-rows then RBN B-rows of 64 B each; one 1 KiB load
-  // covers 16 rows.  Wavefront `wave` issues A loads q = wave*R_DMA_A + i and B loads
-  // q = wave*R_DMA_B + i.  Lane l of a load fills row 16q + l/4, position l%4, with the
-  // row's 16-byte chunk (l%4) ^ swz(row), swz(row) = (row >> 2) & 3.
+  // DMA assignment: a stage holds RBM A-rows of 64 B, then RBN B-rows of B::ROW bytes (64
+  // for bf16, 32 for int8); one 1 KiB load covers 16 A rows or B::RPI B rows.  Wavefront
+  // `wave` issues A loads q = wave*R_DMA_A + i and B loads q = wave*B::DMA + i.  Lane l of
+  // an A load fills row 16q + l/4, 16-byte position l%4, with the row's chunk
+  // (l%4) ^ swz(row), swz(row) = (row >> 2) & 3 (bf16 B rows alike).  Lane l of an int8 B
+  // load fills row 32q + l/2, half l%2, with the row's half (l%2) ^ swz8(row),
+  // swz8(row) = (row >> 3) & 1.  The swizzles keep the operand reads free of bank conflicts.
   const uint16_t* a_src[R_DMA_A];
-  const uint16_t* b_src[R_DMA_B];
-  int ca[R_DMA_A], cb[R_DMA_B];
+  const unsigned char* b_src[B::DMA];
+  int ca[R_DMA_A], cb[B::DMA];
 #pragma unroll
   for (int i = 0; i < R_DMA_A; ++i) {
     const int row = 16 * (wave * R_DMA_A + i) + lane / 4;
@@ -346,28 +374,29 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     a_src[i] = a_row_t<MODE>(a, w, w.m0 + row);
   }
 #pragma unroll
-  for (int i = 0; i < R_DMA_B; ++i) {
-    const int row = 16 * (wave * R_DMA_B + i) + lane / 4;
-    cb[i] = ((lane % 4) ^ ((row >> 2) & 3)) * 8;
-    b_src[i] = reinterpret_cast<const uint16_t*>(b_row_t<MODE, RBN>(a, w, row, 2));
+  for (int i = 0; i < B::DMA; ++i) {
+    const int row = B::RPI * (wave * B::DMA + i) + lane / B::LPR;
+    cb[i] = W8 ? ((lane % 2) ^ ((row >> 3) & 1)) * 16 : ((lane % 4) ^ ((row >> 2) & 3)) * 16;  // bytes
+    b_src[i] = b_row_t<MODE, RBN>(a, w, row, W8 ? 1 : 2);
   }
   auto issue = [&](int kt) {
-    unsigned char* st = rlds + (kt % RNST) * R_STAGE;
+    unsigned char* st = rlds + (kt % RNST) * B::STAGE;
     const int kb = kt * RBK;
 #pragma unroll
     for (int i = 0; i < R_DMA_A; ++i)
       __builtin_amdgcn_global_load_lds((global_void*)(a_src[i] + kb + ca[i]),
                                        (lds_void*)(st + (wave * R_DMA_A + i) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < R_DMA_B; ++i)
-      __builtin_amdgcn_global_load_lds((global_void*)(b_src[i] + kb + cb[i]),
-                                       (lds_void*)(st + R_A_BYTES + (wave * R_DMA_B + i) * 1024), 16,
+    for (int i = 0; i < B::DMA; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(b_src[i] + kb * (W8 ? 1 : 2) + cb[i]),
+                                       (lds_void*)(st + R_A_BYTES + (wave * B::DMA + i) * 1024), 16,
                                        0, 0);
   };
 
   const int wn = wave, lr = lane % 16;
-  // operand reads: row r (a multiple of 16 plus lr), logical chunk c = lane/16 -> byte
-  // offset r*64 + ((c ^ swz(r)) * 16); swz(r) = (lr >> 2) & 3 since r - lr is a multiple of 16
+  // operand reads: row r (a multiple of 16 plus lr), logical chunk c = lane/16 (16 bytes of
+  // bf16, or 8 bytes of int8) -> byte offset r*64 + ((c ^ swz(r)) * 16) for bf16,
+  // r*32 + (((c >> 1) ^ swz8(r)) * 16) + (c & 1) * 8 for int8
   const int rd_chunk = ((lane / 16) ^ ((lr >> 2) & 3)) * 16;
   int a_off[R_TI], b_off[R_TJ];
 #pragma unroll
@@ -379,7 +408,9 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
       row = (j < R_TJ / 2 ? 0 : RBN / 2) + wn * (RBN / RWN / 2) + (j % (R_TJ / 2)) * 16 + lr;
     else
       row = wn * (RBN / RWN) + j * 16 + lr;
-    b_off[j] = R_A_BYTES + row * 64 + rd_chunk;
+    const int c = lane / 16;
+    b_off[j] = R_A_BYTES + (W8 ? row * 32 + (((c >> 1) ^ ((row >> 3) & 1)) * 16) + (c & 1) * 8
+                               : row * 64 + rd_chunk);
   }
   // 16-row slices of the tile that hold rows of the group; the MFMAs of the others (the
   // padding of a group's last tile) are skipped
@@ -401,12 +432,12 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
   auto k_loop = [&](auto live) {
     constexpr int NI = decltype(live)::value;
     for (int kt = 0; kt < nk; ++kt) {
-      // stage kt is complete once at most (stages issued after it) * R_LPS loads are pending
+      // stage kt is complete once at most (stages issued after it) * B::LPS loads are pending
       const int ahead = min(nk - 1, kt + RNST - 2) - kt;
       if (ahead >= 2)
-        wait_vmcnt<2 * R_LPS>();
+        wait_vmcnt<2 * B::LPS>();
       else if (ahead == 1)
-        wait_vmcnt<R_LPS>();
+        wait_vmcnt<B::LPS>();
       else
         wait_vmcnt<0>();
       // Every wavefront waited for its own loads of stage kt above, so after this barrier the
@@ -414,10 +445,12 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
       // s_barrier: __syncthreads() would add a release fence, i.e. wait for all loads in flight.
       asm volatile("s_barrier" ::: "memory");
       if (kt + RNST - 1 < nk) issue(kt + RNST - 1);
-      const unsigned char* st = rlds + (kt % RNST) * R_STAGE;
+      const unsigned char* st = rlds + (kt % RNST) * B::STAGE;
       bf16x8 bfr[R_TJ], af[NI];
 #pragma unroll
-      for (int j = 0; j < R_TJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j]);
+      for (int j = 0; j < R_TJ; ++j)
+        bfr[j] = W8 ? i8x8_to_bf16x8(*reinterpret_cast<const uint2*>(st + b_off[j]))
+                    : *reinterpret_cast<const bf16x8*>(st + b_off[j]);
 #pragma unroll
       for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i]);
 #pragma unroll
@@ -454,7 +487,13 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int j = 0; j < R_TJ / 2; ++j) {
         const int n = w.n0 + wn * (RBN / RWN / 2) + j * 16 + c4;  // N % 16 == 0: all 4 or none
         if (n < N) {
-          const f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
+          f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
+          if (W8) {  // per-channel scales on the fp32 sums
+            const float4 sg = *reinterpret_cast<const float4*>(a.s0 + (size_t)w.g * N + n);
+            const float4 su = *reinterpret_cast<const float4*>(a.s1 + (size_t)w.g * N + n);
+            g = g * f32x4{sg.x, sg.y, sg.z, sg.w};
+            u = u * f32x4{su.x, su.y, su.z, su.w};
+          }
           *reinterpret_cast<uint2*>(orow + n) =
               make_uint2(pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
                          pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]));
@@ -465,7 +504,11 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int j = 0; j < R_TJ; ++j) {
         const int n = w.n0 + wn * (RBN / RWN) + j * 16 + c4;
         if (n < N) {
-          const f32x4 o = acc[i][j];
+          f32x4 o = acc[i][j];
+          if (W8) {
+            const float4 sd = *reinterpret_cast<const float4*>(a.s0 + (size_t)w.g * N + n);
+            o = o * f32x4{sd.x, sd.y, sd.z, sd.w};
+          }
           *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
       }
@@ -482,9 +525,11 @@ hipError_t set_lds(F* kernel, size_t bytes, bool& done) {
   return e;
 }
 
-// The ring kernel serves bf16 weights when both K dimensions are multiples of its K-step;
-// both launches of a layer must use the same M-tile (it is baked into the launch plan).
-bool use_ring(const LayerDims& L) { return L.wdt == MOE_BF16 && L.d % RBK == 0 && L.I % RBK == 0; }
+// The ring kernel serves bf16 and int8 weights when both K dimensions are multiples of its
+// K-step; both launches of a layer must use the same M-tile (it is baked into the launch plan).
+bool use_ring(const LayerDims& L) {
+  return (L.wdt == MOE_BF16 || L.wdt == MOE_I8) && L.d % RBK == 0 && L.I % RBK == 0;
+}
 
 template <int MODE, bool I8>
 hipError_t run_gemm(GemmArgs a, int max_tiles, bool ring, hipStream_t s) {
@@ -495,11 +540,11 @@ hipError_t run_gemm(GemmArgs a, int max_tiles, bool ring, hipStream_t s) {
   int grid = max_tiles * nt;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   hipError_t e;
-  if (ring && !I8) {
+  if (ring) {
     static bool done = false;
-    if ((e = set_lds(&k_gemm_ring<MODE>, R_LDS, done)) != hipSuccess) return e;
+    if ((e = set_lds(&k_gemm_ring<MODE, I8>, RingB<I8>::LDS, done)) != hipSuccess) return e;
     LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-    k_gemm_ring<MODE><<<grid, R_THREADS, R_LDS, s>>>(a);
+    k_gemm_ring<MODE, I8><<<grid, R_THREADS, RingB<I8>::LDS, s>>>(a);
   } else {
     static bool done = false;
     if ((e = set_lds(&k_gemm<MODE, I8>, GEMM_LDS, done)) != hipSuccess) return e;
@@ -538,7 +583,7 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.h;
   a.K = L.d;
   a.N = L.I;
-  err = i8 ? run_gemm<0, true>(a, grid_tiles, false, s) : run_gemm<0, false>(a, grid_tiles, ring, s);
+  err = i8 ? run_gemm<0, true>(a, grid_tiles, ring, s) : run_gemm<0, false>(a, grid_tiles, ring, s);
   if (err != hipSuccess) return err;
 
   a.in = f.h;
@@ -549,7 +594,7 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.rows;
   a.K = L.I;
   a.N = L.d;
-  return i8 ? run_gemm<1, true>(a, grid_tiles, false, s) : run_gemm<1, false>(a, grid_tiles, ring, s);
+  return i8 ? run_gemm<1, true>(a, grid_tiles, ring, s) : run_gemm<1, false>(a, grid_tiles, ring, s);
 }
 
 }  // namespace moe
