@@ -68,9 +68,23 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
   };
   load_slice(e0, 0);  // in flight while the activations are staged
 
+  // token rows -> LDS, eight loads per thread in flight before their stores
   uint4* xs = reinterpret_cast<uint4*>(smem);
   const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)t0 * d);
-  for (int i = threadIdx.x; i < tb * row_chunks; i += blockDim.x) xs[i] = xg[i];
+  const int total = tb * row_chunks;
+  for (int i0 = threadIdx.x; i0 < total; i0 += 8 * blockDim.x) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * blockDim.x;
+      v[u] = i < total ? xg[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * blockDim.x;
+      if (i < total) xs[i] = v[u];
+    }
+  }
   __syncthreads();
 
   for (int ei = 0; ei < epw; ++ei) {
