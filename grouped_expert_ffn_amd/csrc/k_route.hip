@@ -117,12 +117,12 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
   }
 }
 
-// Router logits on the matrix cores, for bf16 layers past decode sizes (E <= 64, d a multiple
-// of 32).  A block owns 16 tokens and all experts; its 8 wavefronts split K into 8 contiguous
-// slices and each accumulates the 16 x 16*NJ partial logits of its slice with
-// v_mfma_f32_16x16x32_bf16, reading both operands straight from global memory (x rows once,
-// the 256 KiB router matrix from L2).  The eight partials are summed in LDS in a fixed order.
-// grid: ceil(T / 16); block 512
+// Router logits on the matrix cores, for bf16 layers past decode sizes (d a multiple of 32).
+// A block owns 16 tokens and 16*NJ experts (blockIdx.y); its 8 wavefronts split K into 8
+// contiguous slices and each accumulates the 16 x 16*NJ partial logits of its slice with
+// v_mfma_f32_16x16x32_bf16, reading both operands straight from global memory (token rows
+// and router rows from L2).  The eight partials are summed in LDS in a fixed order.
+// grid: (ceil(T / 16), ceil(E / (16 * NJ))); block 512
 constexpr int kRouterMfmaWaves = 8;
 template <int NJ>
 __global__ __launch_bounds__(512) void k_router_mfma(int T, int d, int E,
@@ -133,6 +133,7 @@ __global__ __launch_bounds__(512) void k_router_mfma(int T, int d, int E,
   __shared__ float red[kRouterMfmaWaves][16][16 * NJ];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int t0 = blockIdx.x * 16;
+  const int eb = blockIdx.y * 16 * NJ;  // first expert of this block
   const int lr = lane % 16, kc = (lane / 16) * 8;
   const int steps = d / 32;
   const int s0 = wave * steps / kRouterMfmaWaves, s1 = (wave + 1) * steps / kRouterMfmaWaves;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(512) void k_router_mfma(int T, int d, int E,
   const uint16_t* xr = x + (size_t)min(t0 + lr, T - 1) * d + kc;
   const uint16_t* wr[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) wr[j] = w + (size_t)min(16 * j + lr, E - 1) * d + kc;
+  for (int j = 0; j < NJ; ++j) wr[j] = w + (size_t)min(eb + 16 * j + lr, E - 1) * d + kc;
   f32x4 acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -173,10 +174,10 @@ __global__ __launch_bounds__(512) void k_router_mfma(int T, int d, int E,
     for (int v = 0; v < 4; ++v) red[wave][(lane / 16) * 4 + v][16 * j + lr] = acc[j][v];
   __syncthreads();
   for (int i = threadIdx.x; i < 16 * 16 * NJ; i += blockDim.x) {
-    const int tt = i / (16 * NJ), e = i % (16 * NJ);
+    const int tt = i / (16 * NJ), ej = i % (16 * NJ), e = eb + ej;
     if (t0 + tt < T && e < E) {
-      const float sum = ((red[0][tt][e] + red[1][tt][e]) + (red[2][tt][e] + red[3][tt][e])) +
-                        ((red[4][tt][e] + red[5][tt][e]) + (red[6][tt][e] + red[7][tt][e]));
+      const float sum = ((red[0][tt][ej] + red[1][tt][ej]) + (red[2][tt][ej] + red[3][tt][ej])) +
+                        ((red[4][tt][ej] + red[5][tt][ej]) + (red[6][tt][ej] + red[7][tt][ej]));
       logits[(size_t)(t0 + tt) * E + e] = sum + (bias ? bias[e] : 0.f);
     }
   }
@@ -231,24 +232,20 @@ hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, fl
   return hipGetLastError();
 }
 
-// Matrix-core router: bf16, at most 64 experts, K in whole MFMA steps, past decode sizes.
+// Matrix-core router: bf16, K in whole MFMA steps, past decode sizes.
 static bool router_on_mfma(const LayerDims& L, int T) {
-  return L.act == MOE_BF16 && L.E <= 64 && L.d % 32 == 0 && T > kRouterMfmaMinT;
+  return L.act == MOE_BF16 && L.d % 32 == 0 && T > kRouterMfmaMinT;
 }
 
 hipError_t launch_router_logits(const LayerDims& L, int T, const void* x, const void* w_router,
                                 const float* bias, float* logits, hipStream_t s) {
   if (router_on_mfma(L, T)) {
-    const dim3 grid((T + 15) / 16);
-    const uint16_t* xb = (const uint16_t*)x;
-    const uint16_t* wb = (const uint16_t*)w_router;
+    // one 16-expert tile per block (four times the blocks of one block per token group, so
+    // the router reads spread over more CUs)
+    const dim3 grid((T + 15) / 16, (L.E + 15) / 16);
     LaunchTimer timer(MOE_KERNEL_ROUTER, s);
-    switch ((L.E + 15) / 16) {
-      case 1: k_router_mfma<1><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
-      case 2: k_router_mfma<2><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
-      case 3: k_router_mfma<3><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
-      default: k_router_mfma<4><<<grid, 512, 0, s>>>(T, L.d, L.E, xb, wb, bias, logits); break;
-    }
+    k_router_mfma<1><<<grid, 512, 0, s>>>(T, L.d, L.E, (const uint16_t*)x, (const uint16_t*)w_router,
+                                          bias, logits);
     return hipGetLastError();
   }
   const int esz = L.act == MOE_F32 ? 4 : 2;

@@ -404,3 +404,33 @@ def test_forward_with_capacity(wl, T, cf):
     tok = list(range(T)) if T <= 300 else sorted(set(range(0, T, 97)) | {T - 1})
     y_ref = O.moe_layer(x, gl.experts, ids_g, w_ref, wl.S, wl.E, tokens=tok, keep=keep)
     C.assert_close(C.widen_dev(y)[tok], y_ref, wl.act, f"{wl.name} T={T} cf={cf}")
+
+
+# ----------------------------------------------------------------------------------------
+# the layer captured in a HIP graph: every replay equals the eager result bit for bit
+# ----------------------------------------------------------------------------------------
+@pytest.mark.parametrize("wl,T", [(S.OLMOE_BF16, 8), (SMALL_RING, 300), (S.DEEPSEEK_BF16, 16)],
+                         ids=case_id)
+def test_forward_graph_replay_matches_eager(wl, T):
+    from grouped_expert_ffn_amd import abi, to_device
+    t = T_()
+    gl = C.GpuLayer(wl)
+    x = to_device(S.make_tokens(wl, T))
+    x_other = to_device(S.make_tokens(wl, T, seed=5))
+    y_eager = gl.dev.forward(x)
+    t.cuda.synchronize()
+    ws = gl.dev.workspace(T)
+    y_graph = t.empty_like(y_eager)
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        abi.moe_forward(gl.desc, T, x, gl.dev.w_router, gl.dev.bias, gl.dev.weights, None, y_graph,
+                        None, None, ws, ws.numel())
+    for _ in range(4):
+        y_graph.zero_()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert t.equal(y_graph, y_eager)
+        gl.dev.forward(x_other)  # eager work on the same workspace between replays
+        t.cuda.synchronize()
+    del g
