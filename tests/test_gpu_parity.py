@@ -167,7 +167,14 @@ SMALL_ZIPF = dataclasses.replace(SMALL_RAGGED, name="small_zipf", cid=92, routin
 SMALL_RING = S.Workload("small_ring", 93, d=288, E=8, k=2, I=352, S=1, renormalize=True,
                         tokens=(300,))
 
+# the limits of the descriptor: 256 experts, top-16, 8 shared experts, and the smallest
+# dimensions (d = I = 16; neither a multiple of the 32-wide K step of the ring GEMM)
+EDGE_MAX = S.Workload("edge_max", 95, d=48, E=256, k=16, I=48, S=8, renormalize=True,
+                      tokens=(40,))
+EDGE_MIN = S.Workload("edge_min", 96, d=16, E=3, k=1, I=16, S=1, tokens=(40,))
+
 FULL_CASES = [  # every row checked
+    (EDGE_MAX, 4), (EDGE_MAX, 40), (EDGE_MIN, 5), (EDGE_MIN, 40), (S.TINY_F32, 200),
     (S.TINY_F32, 16), (SMALL_RAGGED, 100), (SMALL_RAGGED, 7), (SMALL_RAGGED_I8, 100),
     (SMALL_RAGGED_I8, 5), (SMALL_ZIPF, 300), (SMALL_RING, 300), (SMALL_RING, 40),
     (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8),
