@@ -1,11 +1,12 @@
-// Grouped GEMM on the bf16 matrix cores for prefill sizes: every expert in one launch.
+// Grouped GEMM on the matrix cores for prefill sizes: every expert in one launch.
 //
 // The switchyard page runs all experts' GEMMs in one launch with the SwiGLU fused into the
 // epilogue (§02 "One launch for all experts"); here that is one launch per matrix pair on
 // gfx950's v_mfma_f32_16x16x32_bf16.  Work items come from the launch plan written by the
 // permute kernel: each workgroup maps to one (M-tile, N-tile) of one group, in an XCD-aware
 // order; work past the plan's count exits at once, so the grid can be sized from T*k
-// without reading counts back to the host.
+// without reading counts back to the host.  With a capacity limit in the plan, a routed
+// group counts only its first C rows.
 //
 // Both kernels use 128-row M-tiles.  For gate/up an N-tile holds n gate channels followed by
 // the same n up channels, and every wavefront holds matching gate and up accumulators, so
@@ -13,22 +14,21 @@
 // read in order (h rows).  128 rows keep the padding of the last tile of each expert small
 // under skewed routing, where most experts get a few hundred rows.
 //
-//  * k_gemm_ring (bf16 weights, K a multiple of 32): 128x256 tiles, four wavefronts side by
-//    side each owning 128x64 (32 MFMA tiles), so a group's last, partly filled tile skips
-//    the MFMAs of its empty 16-row slices in every wavefront alike.  The weights are the
-//    first MFMA operand, which leaves 4 consecutive output channels in each lane for 8-byte
-//    stores.  BK=32 and a ring of NST LDS stages
-//    filled directly from global memory by global_load_lds_dwordx4, issued NST-1 stages
-//    ahead of the MFMAs, so several stages of loads are always in flight without holding
-//    registers.  The DMA writes lane l's 16 bytes at base + 16*l, so a stage is row-major
-//    with 64-byte rows; the XOR swizzle that keeps the MFMA operand reads free of bank
-//    conflicts is applied on the source side (each lane fetches a permuted 16-byte chunk
-//    of its row).
-//  * k_gemm (any K, int8 weights): 128x128 tiles, four wavefronts in a 2x2 layout each
-//    owning 64x64.  BK=64, LDS double buffer (rows padded by 16 bytes) with
-//    a register prefetch of the next K-step; int8 weights are widened to bf16 (exact) on
-//    the way into LDS.  The per-channel int8 scale multiplies the fp32 accumulator in the
-//    epilogue.
+//  * k_gemm_ring (bf16 or int8 weights, K a multiple of 32): 128x256 tiles, four wavefronts
+//    side by side each owning 128x64 (32 MFMA tiles), so a group's last, partly filled tile
+//    skips the MFMAs of its empty 16-row slices in every wavefront alike.  The weights are
+//    the first MFMA operand, which leaves 4 consecutive output channels in each lane for
+//    8-byte stores.  BK=32 and a ring of NST LDS stages filled directly from global memory
+//    by global_load_lds_dwordx4, issued NST-1 stages ahead of the MFMAs, so several stages
+//    of loads are always in flight without holding registers.  The DMA writes lane l's 16
+//    bytes at base + 16*l, so a stage is row-major (64-byte bf16 rows; 32-byte int8 weight
+//    rows); the XOR swizzle that keeps the MFMA operand reads free of bank conflicts is
+//    applied on the source side (each lane fetches a permuted 16-byte piece of its row).
+//    int8 weights are widened to bf16 (exact) as they are read from LDS, and the
+//    per-channel scales multiply the fp32 sums in the epilogue.
+//  * k_gemm (any K that is a multiple of 16): 128x128 tiles, four wavefronts in a 2x2 layout
+//    each owning 64x64.  BK=64, LDS double buffer (rows padded by 16 bytes) with a register
+//    prefetch of the next K-step; int8 weights are widened to bf16 on the way into LDS.
 #include <type_traits>
 
 #include "moe_internal.h"

@@ -3,8 +3,8 @@
 //
 // One workgroup of 16 wavefronts.  The expert ids are first staged in LDS (every thread
 // issues all of its loads before the first store, so the staging costs one memory round
-// trip rather than one per step; the fused kernel writes them there from its top-k).  Wavefront w owns a contiguous range of flat rows, walked
-// 64 at a time.  Inside a step, lanes holding the same expert id find each other with eight
+// trip rather than one per step; the fused kernel writes them there from its top-k).
+// Wavefront w owns a contiguous range of flat rows, walked 64 at a time.  Inside a step, lanes holding the same expert id find each other with eight
 // ballots (one per bit of the id); the lowest such lane is the group's leader and the rank
 // of a lane among its peers is a popcount of the lower peers.  Pass 1 builds a per-wavefront
 // histogram in LDS (only leaders write, and no two leaders share an address), a column scan

@@ -1,11 +1,12 @@
 // Router logits, top-k gating and the RMSNorm prologue.
 //
-// Router: logits[t,e] = sum_c x[t,c] W_r[e,c] + b[e] with fp32 accumulation.  A block of four
-// wavefronts stages a few token rows in LDS; each wavefront first issues the loads of a whole
-// W_r row (16 bytes per lane per load, all in flight together), then reduces with DPP.  At
-// decode sizes every wavefront owns one expert (many small blocks, so the router matrix is
-// read by many CUs at once); at prefill sizes a block owns all experts for its tokens and
-// prefetches the next expert's row while reducing the current one.
+// Router: logits[t,e] = sum_c x[t,c] W_r[e,c] + b[e] with fp32 accumulation.  Past 64 tokens,
+// bf16 layers whose d is a multiple of 32 use the matrix cores (k_router_mfma below).
+// Otherwise a block of four wavefronts stages a few token rows in LDS; each wavefront first
+// issues the loads of a whole W_r row (16 bytes per lane per load, all in flight together),
+// then reduces with DPP.  Up to 64 tokens every wavefront owns one expert (many small
+// blocks, so the router matrix is read by many CUs at once); beyond, a block owns all
+// experts for its tokens and prefetches the next expert's row while reducing the current.
 //
 // Top-k: one wavefront per token (the switchyard page routes each token in one warp, §02
 // "Route and sort").  Each lane holds up to four logits; k rounds of wave-wide max / min
