@@ -29,6 +29,7 @@
 //  * k_gemm (any K that is a multiple of 16): 128x128 tiles, four wavefronts in a 2x2 layout
 //    each owning 64x64.  BK=64, LDS double buffer (rows padded by 16 bytes) with a register
 //    prefetch of the next K-step; int8 weights are widened to bf16 on the way into LDS.
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -516,12 +517,20 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
   }
 }
 
+// Raise a kernel's dynamic-LDS limit once per device (the attribute belongs to the current
+// device; the flags are indexed by device ordinal and safe to race on).
+constexpr int kMaxDevices = 64;
+typedef std::atomic<bool> LdsFlags[kMaxDevices];
 template <typename F>
-hipError_t set_lds(F* kernel, size_t bytes, bool& done) {
-  if (done) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done = true;
+hipError_t set_lds(F* kernel, size_t bytes, LdsFlags& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
   return e;
 }
 
@@ -541,12 +550,12 @@ hipError_t run_gemm(GemmArgs a, int max_tiles, bool ring, hipStream_t s) {
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   hipError_t e;
   if (ring) {
-    static bool done = false;
+    static LdsFlags done;
     if ((e = set_lds(&k_gemm_ring<MODE, I8>, RingB<I8>::LDS, done)) != hipSuccess) return e;
     LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
     k_gemm_ring<MODE, I8><<<grid, R_THREADS, RingB<I8>::LDS, s>>>(a);
   } else {
-    static bool done = false;
+    static LdsFlags done;
     if ((e = set_lds(&k_gemm<MODE, I8>, GEMM_LDS, done)) != hipSuccess) return e;
     LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
     k_gemm<MODE, I8><<<grid, THREADS, GEMM_LDS, s>>>(a);
