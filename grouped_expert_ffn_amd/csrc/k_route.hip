@@ -200,25 +200,100 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int k, int renorm,
   topk_select(l, E, k, renorm, lane, ids, wout, t, nullptr);
 }
 
-// y = x / sqrt(mean(x^2) + eps), one block per token, fp32 sums in a fixed order
-template <typename AT>
+// 16-byte chunks of a row (8 bf16 or 4 fp32) as floats and back
+template <typename AT> struct Chunk;
+template <> struct Chunk<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const uint4& c, float (&f)[8]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = bf16_lo(w[q]);
+      f[2 * q + 1] = bf16_hi(w[q]);
+    }
+  }
+  __device__ static uint4 pack(const float (&f)[8]) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+  }
+};
+template <> struct Chunk<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(const uint4& c, float (&f)[4]) {
+    f[0] = __uint_as_float(c.x);
+    f[1] = __uint_as_float(c.y);
+    f[2] = __uint_as_float(c.z);
+    f[3] = __uint_as_float(c.w);
+  }
+  __device__ static uint4 pack(const float (&f)[4]) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+// y = x / sqrt(mean(x^2) + eps), one block per token, fp32 sums in a fixed order.  Rows are
+// whole 16-byte chunks at 16-byte aligned addresses; each thread loads its (at most R) chunks
+// once, keeps them in registers for the sum of squares and the scaling, and writes 16-byte
+// stores.
+template <typename AT, int R>
 __global__ __launch_bounds__(256) void k_rmsnorm(int d, float eps, const AT* __restrict__ x,
-                                                 AT* __restrict__ y) {
+                                                   AT* __restrict__ y) {
+  using C = Chunk<AT>;
   __shared__ float part[4];
   const int t = blockIdx.x;
-  const AT* xr = x + (size_t)t * d;
-  AT* yr = y + (size_t)t * d;
+  const int nc = d / C::N;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * d);
+  uint4* yr = reinterpret_cast<uint4*>(y + (size_t)t * d);
+  uint4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = threadIdx.x + 256 * r;
+    v[r] = c < nc ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    const float v = Act<AT>::load(xr, c);
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float f[C::N];
+    C::unpack(v[r], f);
+#pragma unroll
+    for (int q = 0; q < C::N; ++q) ss = fmaf(f[q], f[q], ss);
   }
   ss = wave_sum_u(ss);
   if (threadIdx.x % kWave == 0) part[threadIdx.x / kWave] = ss;
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += blockDim.x) Act<AT>::store(yr, c, Act<AT>::load(xr, c) * inv);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = threadIdx.x + 256 * r;
+    if (c < nc) {
+      float f[C::N];
+      C::unpack(v[r], f);
+#pragma unroll
+      for (int q = 0; q < C::N; ++q) f[q] *= inv;
+      yr[c] = C::pack(f);
+    }
+  }
+}
+
+template <typename AT>
+hipError_t rmsnorm_typed(int T, int d, const AT* x, AT* y, float eps, hipStream_t s) {
+  constexpr int N = Chunk<AT>::N;
+  const int per_thread = (d / N + 255) / 256;  // 16-byte chunks per thread
+  // the descriptor and pointer checks guarantee d % 16 == 0, d <= 16384 and aligned rows
+  if (d % N != 0 || (((uintptr_t)x | (uintptr_t)y) & 15) != 0 || per_thread > 16)
+    return hipErrorInvalidValue;
+  if (per_thread <= 1)
+    k_rmsnorm<AT, 1><<<T, 256, 0, s>>>(d, eps, x, y);
+  else if (per_thread <= 2)
+    k_rmsnorm<AT, 2><<<T, 256, 0, s>>>(d, eps, x, y);
+  else if (per_thread <= 4)
+    k_rmsnorm<AT, 4><<<T, 256, 0, s>>>(d, eps, x, y);
+  else if (per_thread <= 8)
+    k_rmsnorm<AT, 8><<<T, 256, 0, s>>>(d, eps, x, y);
+  else
+    k_rmsnorm<AT, 16><<<T, 256, 0, s>>>(d, eps, x, y);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -226,11 +301,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(int d, float eps, const AT* __r
 hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, float eps,
                           hipStream_t s) {
   LaunchTimer timer(MOE_KERNEL_RMSNORM, s);
-  if (L.act == MOE_F32)
-    k_rmsnorm<float><<<T, 256, 0, s>>>(L.d, eps, (const float*)x, (float*)xn);
-  else
-    k_rmsnorm<uint16_t><<<T, 256, 0, s>>>(L.d, eps, (const uint16_t*)x, (uint16_t*)xn);
-  return hipGetLastError();
+  if (L.act == MOE_F32) return rmsnorm_typed<float>(T, L.d, (const float*)x, (float*)xn, eps, s);
+  return rmsnorm_typed<uint16_t>(T, L.d, (const uint16_t*)x, (uint16_t*)xn, eps, s);
 }
 
 // Matrix-core router: bf16, K in whole MFMA steps, past decode sizes.

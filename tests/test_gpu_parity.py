@@ -344,6 +344,37 @@ def test_stack_staged_per_layer():
     assert 3.9 <= skews[0] <= 4.1, skews
 
 
+# RMSNorm prologue at every register width of its kernel (1, 2, 4, 8 and 16 chunks of 16
+# bytes per thread, whole and with a partial last round) for both activation types
+PRE_NORM_CASES = [("bf16", 48), ("bf16", 4096), ("bf16", 6144), ("bf16", 16384),
+                  ("f32", 48), ("f32", 2048), ("f32", 12288), ("f32", 16384)]
+
+
+@pytest.mark.parametrize("act,d", PRE_NORM_CASES, ids=[f"{a}-d{d}" for a, d in PRE_NORM_CASES])
+def test_forward_pre_norm_widths(act, d):
+    from grouped_expert_ffn_amd import DeviceLayer, to_device
+    t = T_()
+    T = 6
+    wl = S.Workload(f"pre_norm_{act}_{d}", 97, d=d, E=4, k=2, I=16, act=act, wdt=act,
+                    pre_norm=True, tokens=(T,))
+    host = S.make_layer(wl, 0)
+    dl = DeviceLayer(C.desc_of(wl), host.w_router, host.bias, host.w_gate, host.w_up, host.w_down)
+    x_host = S.make_tokens(wl, T)
+    ids = t.empty((T, wl.k), dtype=t.int32, device="cuda")
+    y = dl.forward(to_device(x_host), topk_ids=ids)
+    t.cuda.synchronize()
+    if act == "bf16":
+        xn, delta = O.stack_layer_input(x_host, wl.norm_eps), C.TIE_DELTA_STACK
+    else:
+        xn, delta = O.rmsnorm(x_host, wl.norm_eps), C.TIE_DELTA
+    logits = O.router_logits(xn, host.w_router, host.bias)
+    ids_g = ids.cpu().numpy()
+    C.check_routing_against_oracle(ids_g, logits, wl.k, delta)
+    w_ref = O.gate_weights_for(logits, ids_g, wl.renormalize)
+    ref = O.moe_layer(xn, O.Experts.from_layer(host), ids_g, w_ref, 0, wl.E)
+    C.assert_close(C.widen_dev(y), ref, act, f"pre_norm {act} d={d}")
+
+
 # ----------------------------------------------------------------------------------------
 # option: capacity-factor dropping
 # ----------------------------------------------------------------------------------------
