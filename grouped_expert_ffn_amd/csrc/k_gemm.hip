@@ -14,9 +14,10 @@
 // read in order (h rows).  128 rows keep the padding of the last tile of each expert small
 // under skewed routing, where most experts get a few hundred rows.
 //
-//  * k_gemm_ring (bf16 or int8 weights, K a multiple of 32): 128x256 tiles, four wavefronts
-//    side by side each owning 128x64 (32 MFMA tiles), so a group's last, partly filled tile
-//    skips the MFMAs of its empty 16-row slices in every wavefront alike.  The weights are
+//  * k_gemm_ring (bf16 or int8 weights, K a multiple of 32): 128x256 tiles, or 128x128 where
+//    a tuned rule picks them (ring_tile_n below).  Four wavefronts side by side each own all
+//    128 rows and a quarter of the columns, so a group's last, partly filled tile skips the
+//    MFMAs of its empty 16-row slices in every wavefront alike.  The weights are
 //    the first MFMA operand, which leaves 4 consecutive output channels in each lane for
 //    8-byte stores.  BK=32 and a ring of NST LDS stages filled directly from global memory
 //    by global_load_lds_dwordx4, issued NST-1 stages ahead of the MFMAs, so several stages
@@ -312,26 +313,31 @@ __device__ __forceinline__ void wait_vmcnt() {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
 
-// Tile RBM x RBN (gate/up: RBN/2 gate + the same RBN/2 up channels); four wavefronts side by
-// side, each owning all RBM rows and RBN/4 columns (gate/up: RBN/8 gate + the same up
-// channels); K advances RBK=32 per stage through an RNST-deep ring.
-constexpr int RBM = 128, RBN = 256, RWN = 4;
+// Tile RBM x TBN (gate/up: TBN/2 gate + the same TBN/2 up channels), TBN = 256 or 128; four
+// wavefronts side by side, each owning all RBM rows and TBN/4 columns (gate/up: TBN/8 gate +
+// the same up channels); K advances RBK=32 per stage through an RNST-deep ring.
+constexpr int RBM = 128, RWN = 4;
 constexpr int R_THREADS = 64 * RWN;
-constexpr int R_TI = RBM / 16, R_TJ = RBN / RWN / 16;  // 16x16 MFMA tiles per wavefront
+constexpr int R_TI = RBM / 16;  // 16-row MFMA slices per tile
 constexpr int R_A_BYTES = RBM * RBK * 2;
 constexpr int R_DMA_A = RBM / 16 / RWN;  // A loads per stage per wavefront
 
-// Stage geometry for bf16 (W8 = false) or int8 (W8 = true) weights: B rows of RBK weights.
-template <bool W8>
+// Stage geometry for bf16 (W8 = false) or int8 (W8 = true) weights: TBN B rows of RBK weights.
+template <bool W8, int TBN>
 struct RingB {
+  static constexpr int TJ = TBN / RWN / 16;               // 16-column MFMA tiles per wavefront
   static constexpr int ROW = RBK * (W8 ? 1 : 2);          // bytes per B row per stage
-  static constexpr int BYTES = RBN * ROW;
+  static constexpr int BYTES = TBN * ROW;
   static constexpr int STAGE = R_A_BYTES + BYTES;
   static constexpr int LPR = ROW / 16;                     // DMA lanes per B row
   static constexpr int RPI = 64 / LPR;                     // B rows per DMA load
-  static constexpr int DMA = RBN / RPI / RWN;              // B loads per stage per wavefront
+  static constexpr int DMA = TBN / RPI / RWN;              // B loads per stage per wavefront
   static constexpr int LPS = R_DMA_A + DMA;                // loads per stage per wavefront
   static constexpr size_t LDS = (size_t)RNST * STAGE;
+  // waves per SIMD the registers are sized for: 2 with 32 accumulator tiles per wavefront,
+  // 3 with 16 when the LDS holds three workgroups per CU (160 KiB)
+  static constexpr int WAVES_PER_EU = (TJ == 2 && 160 * 1024 / LDS >= 3) ? 3 : 2;
+  static_assert(DMA * RPI * RWN == TBN && TJ % 2 == 0, "tile split");
   static_assert((RNST - 2) * LPS < 16, "vmcnt range");
 };
 
@@ -348,17 +354,18 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(const uint2& q) {
   return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-template <int MODE, bool W8>
-__global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_ring(
-    const GemmArgs a) {
-  using B = RingB<W8>;
+template <int MODE, bool W8, int TBN>
+__global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
+    RingB<W8, TBN>::WAVES_PER_EU))) void k_gemm_ring(const GemmArgs a) {
+  using B = RingB<W8, TBN>;
+  constexpr int R_TJ = B::TJ;
   extern __shared__ __align__(16) unsigned char rlds[];
   Work w;
   if (!map_work_t<RBM>(a, w)) return;
   const int K = a.K;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
-  // DMA assignment: a stage holds RBM A-rows of 64 B, then RBN B-rows of B::ROW bytes (64
+  // DMA assignment: a stage holds RBM A-rows of 64 B, then TBN B-rows of B::ROW bytes (64
   // for bf16, 32 for int8); one 1 KiB load covers 16 A rows or B::RPI B rows.  Wavefront
   // `wave` issues A loads q = wave*R_DMA_A + i and B loads q = wave*B::DMA + i.  Lane l of
   // an A load fills row 16q + l/4, 16-byte position l%4, with the row's chunk
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int i = 0; i < B::DMA; ++i) {
     const int row = B::RPI * (wave * B::DMA + i) + lane / B::LPR;
     cb[i] = W8 ? ((lane % 2) ^ ((row >> 3) & 1)) * 16 : ((lane % 4) ^ ((row >> 2) & 3)) * 16;  // bytes
-    b_src[i] = b_row_t<MODE, RBN>(a, w, row, W8 ? 1 : 2);
+    b_src[i] = b_row_t<MODE, TBN>(a, w, row, W8 ? 1 : 2);
   }
   auto issue = [&](int kt) {
     unsigned char* st = rlds + (kt % RNST) * B::STAGE;
@@ -406,9 +413,9 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int j = 0; j < R_TJ; ++j) {
     int row;
     if (MODE == 0)  // first half of the tiles: gate channels, second half: the same up channels
-      row = (j < R_TJ / 2 ? 0 : RBN / 2) + wn * (RBN / RWN / 2) + (j % (R_TJ / 2)) * 16 + lr;
+      row = (j < R_TJ / 2 ? 0 : TBN / 2) + wn * (TBN / RWN / 2) + (j % (R_TJ / 2)) * 16 + lr;
     else
-      row = wn * (RBN / RWN) + j * 16 + lr;
+      row = wn * (TBN / RWN) + j * 16 + lr;
     const int c = lane / 16;
     b_off[j] = R_A_BYTES + (W8 ? row * 32 + (((c >> 1) ^ ((row >> 3) & 1)) * 16) + (c & 1) * 8
                                : row * 64 + rd_chunk);
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     if (MODE == 0) {
 #pragma unroll
       for (int j = 0; j < R_TJ / 2; ++j) {
-        const int n = w.n0 + wn * (RBN / RWN / 2) + j * 16 + c4;  // N % 16 == 0: all 4 or none
+        const int n = w.n0 + wn * (TBN / RWN / 2) + j * 16 + c4;  // N % 16 == 0: all 4 or none
         if (n < N) {
           f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
           if (W8) {  // per-channel scales on the fp32 sums
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     } else {
 #pragma unroll
       for (int j = 0; j < R_TJ; ++j) {
-        const int n = w.n0 + wn * (RBN / RWN) + j * 16 + c4;
+        const int n = w.n0 + wn * (TBN / RWN) + j * 16 + c4;
         if (n < N) {
           f32x4 o = acc[i][j];
           if (W8) {
@@ -540,27 +547,64 @@ bool use_ring(const LayerDims& L) {
   return (L.wdt == MOE_BF16 || L.wdt == MOE_I8) && L.d % RBK == 0 && L.I % RBK == 0;
 }
 
+template <int MODE, bool I8, int TBN>
+hipError_t run_ring(const GemmArgs& a, int grid, hipStream_t s) {
+  using B = RingB<I8, TBN>;
+  static LdsFlags done;
+  hipError_t e = set_lds(&k_gemm_ring<MODE, I8, TBN>, B::LDS, done);
+  if (e != hipSuccess) return e;
+  LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
+  k_gemm_ring<MODE, I8, TBN><<<grid, R_THREADS, B::LDS, s>>>(a);
+  return hipGetLastError();
+}
+
+// tbn: N-tile width of the ring kernel (256 or 128), 0 for the general kernel
 template <int MODE, bool I8>
-hipError_t run_gemm(GemmArgs a, int max_tiles, bool ring, hipStream_t s) {
-  const int tbn = ring ? RBN : BN;
-  a.n_blk = MODE == 0 ? tbn / 2 : tbn;
+hipError_t run_gemm(GemmArgs a, int max_tiles, int tbn, hipStream_t s) {
+  const int width = tbn ? tbn : BN;
+  a.n_blk = MODE == 0 ? width / 2 : width;
   const int nt = (a.N + a.n_blk - 1) / a.n_blk;
   // one workgroup per possible (M-tile, N-tile), rounded up to a multiple of the XCD count
   int grid = max_tiles * nt;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
-  hipError_t e;
-  if (ring) {
-    static LdsFlags done;
-    if ((e = set_lds(&k_gemm_ring<MODE, I8>, RingB<I8>::LDS, done)) != hipSuccess) return e;
-    LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-    k_gemm_ring<MODE, I8><<<grid, R_THREADS, RingB<I8>::LDS, s>>>(a);
-  } else {
-    static LdsFlags done;
-    if ((e = set_lds(&k_gemm<MODE, I8>, GEMM_LDS, done)) != hipSuccess) return e;
-    LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-    k_gemm<MODE, I8><<<grid, THREADS, GEMM_LDS, s>>>(a);
-  }
+  if (tbn == 256) return run_ring<MODE, I8, 256>(a, grid, s);
+  if (tbn == 128) return run_ring<MODE, I8, 128>(a, grid, s);
+  static LdsFlags done;
+  hipError_t e = set_lds(&k_gemm<MODE, I8>, GEMM_LDS, done);
+  if (e != hipSuccess) return e;
+  LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
+  k_gemm<MODE, I8><<<grid, THREADS, GEMM_LDS, s>>>(a);
   return hipGetLastError();
+}
+
+// Tuned N-tile widths of the ring kernel.  A rule names one layer shape and the token ranges in
+// which the 128-wide tile beat the 256-wide one on MI355X, for the gate/up and the down matrix
+// separately, measured under the shape's skewed (Zipf) routing and kept only where two sweeps
+// agreed by at least 5%.  Every other shape and token count uses 256.  Under skew the big
+// groups (shared experts, popular routed experts) dominate a launch; narrower tiles split
+// their work over twice the workgroups, at the price of reading each activation tile twice
+// as often, which loses once most groups fill several M-tiles.
+struct TokenRange {
+  int lo, hi;  // inclusive; lo > hi = empty
+};
+struct TileRule {
+  int d, I, E, k, S, wdt;
+  TokenRange gate_up[2], down[2];
+};
+constexpr TileRule kTileRules[] = {
+    // DeepSeek-MoE-shaped layer: 64 routed experts of width 1408, top-6, 2 shared, d = 2048
+    {2048, 1408, 64, 6, 2, MOE_BF16, {{17, 64}, {128, 384}}, {{64, 128}, {384, 512}}},
+    {2048, 1408, 64, 6, 2, MOE_I8, {{17, 32}, {1, 0}}, {{9, 128}, {1, 0}}},
+};
+
+// N-tile width of the ring kernel for one matrix (mode 0 gate/up, 1 down) of a layer at T tokens.
+int ring_tile_n(const LayerDims& L, int T, int mode) {
+  for (const TileRule& r : kTileRules) {
+    if (r.d != L.d || r.I != L.I || r.E != L.E || r.k != L.k || r.S != L.S || r.wdt != L.wdt) continue;
+    for (const TokenRange& t : mode == 0 ? r.gate_up : r.down)
+      if (T >= t.lo && T <= t.hi) return 128;
+  }
+  return 256;
 }
 
 }  // namespace
@@ -592,7 +636,8 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.h;
   a.K = L.d;
   a.N = L.I;
-  err = i8 ? run_gemm<0, true>(a, grid_tiles, ring, s) : run_gemm<0, false>(a, grid_tiles, ring, s);
+  int tbn = ring ? ring_tile_n(L, T, 0) : 0;
+  err = i8 ? run_gemm<0, true>(a, grid_tiles, tbn, s) : run_gemm<0, false>(a, grid_tiles, tbn, s);
   if (err != hipSuccess) return err;
 
   a.in = f.h;
@@ -603,7 +648,8 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.rows;
   a.K = L.I;
   a.N = L.d;
-  return i8 ? run_gemm<1, true>(a, grid_tiles, ring, s) : run_gemm<1, false>(a, grid_tiles, ring, s);
+  tbn = ring ? ring_tile_n(L, T, 1) : 0;
+  return i8 ? run_gemm<1, true>(a, grid_tiles, tbn, s) : run_gemm<1, false>(a, grid_tiles, tbn, s);
 }
 
 }  // namespace moe

@@ -187,6 +187,8 @@ SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     (S.OLMOE_BF16, 64), (S.OLMOE_I8, 64), (S.OLMOE_I8_ZIPF, 64), (S.DEEPSEEK_BF16, 16),
     (S.DEEPSEEK_BF16, 128), (S.DEEPSEEK_BF16, 512), (S.DEEPSEEK_BF16, 2048), (S.DEEPSEEK_I8, 16),
     (S.DEEPSEEK_I8, 512),
+    # the tuned tile widths: gate/up 128 + down 256, gate/up 256 + down 128 (bf16 and int8)
+    (S.DEEPSEEK_BF16, 40), (S.DEEPSEEK_BF16, 450), (S.DEEPSEEK_I8, 24), (S.DEEPSEEK_I8, 100),
 ]
 
 
