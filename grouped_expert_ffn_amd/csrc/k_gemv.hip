@@ -13,7 +13,8 @@
 //  * every weight load of the block is issued at once into registers before any math
 //    (about 16 x 16 B per lane), so a block costs about one memory round trip and several
 //    blocks per CU overlap theirs; the weights then stay in registers while the group's
-//    activation rows are processed in chunks of up to MB rows staged in LDS;
+//    activation rows are processed in chunks of up to MB rows staged in LDS, by
+//    direct-to-LDS loads issued right behind the weights so that both round trips overlap;
 //  * partial sums are reduced over the 8 lanes with DPP moves and over the 4 wavefronts
 //    through LDS in a fixed order, so results are bit-reproducible;
 //  * the epilogue applies the int8 per-channel scale, the SwiGLU (gate/up) and the
@@ -44,6 +45,16 @@ struct GemvArgs {
 
 constexpr int kMB = 8;  // max rows per chunk
 constexpr int kWaves = 4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gmem_void;
+// read-only for the kernel's lifetime (the sort wrote it in an earlier launch): through the
+// constant address space a wave-uniform lookup becomes a scalar load even after the kernel's
+// own stores, so it does not wait behind the vector loads in flight
+typedef const __attribute__((address_space(4))) int32_t cint32;
+// s_waitcnt immediates: only lgkmcnt = 0 (vmcnt and expcnt left at their maxima), only vmcnt = 0
+constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int kWaitVm0 = 0x0F70;
 
 template <typename WT> struct WTraits;
 template <> struct WTraits<float> { static constexpr int V = 4; };  // weights per 16-byte load
@@ -186,21 +197,35 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
               wbuf[c][t][it] = ok ? *reinterpret_cast<const uint4*>(wp[c][t] + col) : make_uint4(0, 0, 0, 0);
         }
       }
-      // (2) activation rows m0 .. m0+mb-1, columns of this round -> LDS
-      __syncthreads();
-      const int chunks = cols * (int)sizeof(AT) / 16;
-      for (int i = threadIdx.x; i < mb * chunks; i += blockDim.x) {
-        const int m = i / chunks, cc = i % chunks;
+      // (2) activation rows m0 .. m0+mb-1, columns of this round -> LDS by direct-to-LDS
+      //     loads (one instruction moves 64 chunks of 16 bytes of one row; no registers),
+      //     issued right behind the weights.  The row lookups are wave-uniform scalar loads,
+      //     so nothing here waits for the weights: the barrier that keeps the previous row
+      //     chunk's LDS reads ahead of the new rows needs only those reads (lgkmcnt), not the
+      //     loads in flight, which __syncthreads() would wait for.
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      asm volatile("s_barrier" ::: "memory");
+      const int chunks = cols * (int)sizeof(AT) / 16;  // per row
+      const int ipr = (chunks + kWave - 1) / kWave;     // instructions per row
+      // wave index made visibly uniform, so the lookups below become scalar loads
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      for (int j = wave_u; j < mb * ipr; j += kWaves) {
+        const int m = j / ipr, c0 = (j % ipr) * kWave;
         const int r = r0 + m0 + m;
         size_t src_row;
         if (MODE == 0)
-          src_row = (g < a.E) ? (size_t)(a.perm[r] / a.k) : (size_t)(m0 + m);
+          src_row = (g < a.E) ? (size_t)(((const cint32*)a.perm)[r] / a.k) : (size_t)(m0 + m);
         else
           src_row = (size_t)r;
-        reinterpret_cast<uint4*>(xs + m * row_bytes)[cc] =
-            reinterpret_cast<const uint4*>(in + src_row * K + k_round)[cc];
+        const int cc = c0 + lane;
+        if (cc < chunks)  // lane cc's 16 bytes land at the instruction's LDS base + 16 * lane
+          __builtin_amdgcn_global_load_lds(
+              (gmem_void*)(in + src_row * K + k_round + cc * (16 / (int)sizeof(AT))),
+              (lds_void*)(xs + m * row_bytes + c0 * 16), 16, 0, 0);
       }
-      __syncthreads();
+      // this wavefront's weights and rows are in; the barrier makes every wavefront's rows visible
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      asm volatile("s_barrier" ::: "memory");
       // (3) math
 #pragma unroll
       for (int it = 0; it < MAXIT; ++it) {
