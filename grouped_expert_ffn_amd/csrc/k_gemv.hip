@@ -40,10 +40,9 @@ struct GemvArgs {
   const int32_t* plan;
   void* out;        // [R, N]
   int K, N, k, E;
-  int mb_max;       // rows staged per chunk (<= kMB)
+  int mb_max;       // rows staged per chunk (<= the kernel's MB)
 };
 
-constexpr int kMB = 8;  // max rows per chunk
 constexpr int kWaves = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -126,12 +125,14 @@ template <> struct Dot<uint16_t, int8_t> {
 
 // MODE 0: h = silu(W0 x) * (W1 x);  MODE 1: out = W0 h
 // CPG: channels per 8-lane group (NB = 8 * CPG channels per block);
-// MAXIT: K steps (8 lanes x 16 B) per wavefront per round.
+// MAXIT: K steps (8 lanes x 16 B) per wavefront per round;
+// MB: rows per chunk (a group with more rows takes further chunks: with one round over K the
+// weights stay in registers, so a small MB costs no traffic and saves accumulator registers).
 // grid: (ceil(N / NB), slots); block 256; dynamic LDS mb_max * ROUND * sizeof(AT).
 // blockIdx.x is dispatched fastest, so the blocks in flight read consecutive N-blocks of
 // one expert: one contiguous stretch of memory streamed in order (measured 25% faster
 // than spreading the blocks in flight over many experts at the same offset).
-template <int MODE, typename AT, typename WT, int CPG, int MAXIT>
+template <int MODE, typename AT, typename WT, int CPG, int MAXIT, int MB>
 __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   constexpr int NB = 8 * CPG;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   constexpr int ROUND = kWaves * MAXIT * STEP;  // K elements per round
   typedef Dot<AT, WT> D;
   extern __shared__ __align__(16) unsigned char xs[];
-  __shared__ float red[kWaves][CPG][NMAT][kMB][8];
+  __shared__ float red[kWaves][CPG][NMAT][MB][8];
 
   const int slot = blockIdx.y;
   if (slot >= a.plan[0]) return;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   }
 
   uint4 wbuf[CPG][NMAT][MAXIT];
-  float acc[CPG][NMAT][kMB];
+  float acc[CPG][NMAT][MB];
   for (int m0 = 0; m0 < M; m0 += a.mb_max) {
     const int mb = min(a.mb_max, M - m0);
 #pragma unroll
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
 #pragma unroll
       for (int t = 0; t < NMAT; ++t)
 #pragma unroll
-        for (int m = 0; m < kMB; ++m) acc[c][t][m] = 0.f;
+        for (int m = 0; m < MB; ++m) acc[c][t][m] = 0.f;
 
     for (int rd = 0; rd < rounds; ++rd) {
       const int k_round = rd * ROUND;
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
             for (int t = 0; t < NMAT; ++t) {
               const typename D::W w = D::prep(wbuf[c][t][it]);
 #pragma unroll
-              for (int m = 0; m < kMB; ++m)
+              for (int m = 0; m < MB; ++m)
                 if (m < mb) acc[c][t][m] = D::run(w, xp + m * row_bytes, acc[c][t][m]);
             }
         }
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
 #pragma unroll
       for (int t = 0; t < NMAT; ++t)
 #pragma unroll
-        for (int m = 0; m < kMB; ++m) {
+        for (int m = 0; m < MB; ++m) {
           const float v = sum8(acc[c][t][m]);
           if (m == q) red[wave][c][t][m][lg] = v;
         }
@@ -286,30 +287,34 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   }
 }
 
-template <int MODE, typename AT, typename WT, int CPG, int MAXIT>
-hipError_t run_gemv(const GemvArgs& a, int slots, hipStream_t s) {
+template <int MODE, typename AT, typename WT, int CPG, int MAXIT, int MB>
+hipError_t run_gemv(GemvArgs a, int T, int slots, hipStream_t s) {
   constexpr int V = WTraits<WT>::V;
   constexpr int ROUND = kWaves * MAXIT * 8 * V;
+  a.mb_max = T < MB ? T : MB;  // no group holds more than T rows
   dim3 grid((a.N + 8 * CPG - 1) / (8 * CPG), slots);
   const size_t lds = (size_t)a.mb_max * ROUND * sizeof(AT);
   LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-  k_gemv<MODE, AT, WT, CPG, MAXIT><<<grid, 256, lds, s>>>(a);
+  k_gemv<MODE, AT, WT, CPG, MAXIT, MB><<<grid, 256, lds, s>>>(a);
   return hipGetLastError();
 }
 
 // Pick MAXIT (K steps per wavefront) so one round covers K when possible, and CPG (channel
 // groups per block).  Measured on the OLMoE shapes: more, smaller blocks beat fewer blocks
 // with more loads per lane once a block's loads fill a round trip, so the down projection
-// uses 2 channel groups and int8 gate/up 1 (a lane's 16 bytes hold twice the weights).
+// uses 2 channel groups and int8 gate/up 1 (a lane's 16 bytes hold twice the weights).  Rows
+// go in chunks of 4 when one round covers K (the registers saved raise the occupancy the
+// bandwidth follows), else of 8 (each further chunk would read the weights again).
 template <int MODE, typename AT, typename WT>
-hipError_t dispatch_gemv(const GemvArgs& a, int slots, hipStream_t s) {
+hipError_t dispatch_gemv(const GemvArgs& a, int T, int slots, hipStream_t s) {
   constexpr int V = WTraits<WT>::V;
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   const int steps = (a.K + 8 * V - 1) / (8 * V);
   const int spw = (steps + kWaves - 1) / kWaves;
-  if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 2), 2>(a, slots, s);
-  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 2 && V == 16 ? 1 : 2), 4>(a, slots, s);
-  return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8>(a, slots, s);
+  if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 2), 2, 4>(a, T, slots, s);
+  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 2 && V == 16 ? 1 : 2), 4, 4>(a, T, slots, s);
+  if (spw <= 8) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8, 4>(a, T, slots, s);
+  return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8, 8>(a, T, slots, s);
 }
 
 }  // namespace
@@ -322,7 +327,6 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.plan = f.plan;
   a.k = L.k;
   a.E = L.E;
-  a.mb_max = T < kMB ? T : kMB;  // no group holds more than T rows
   hipError_t err;
 
   // gate/up + SwiGLU
@@ -335,11 +339,11 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.K = L.d;
   a.N = L.I;
   if (L.act == MOE_F32)
-    err = dispatch_gemv<0, float, float>(a, slots, s);
+    err = dispatch_gemv<0, float, float>(a, T, slots, s);
   else if (L.wdt == MOE_I8)
-    err = dispatch_gemv<0, uint16_t, int8_t>(a, slots, s);
+    err = dispatch_gemv<0, uint16_t, int8_t>(a, T, slots, s);
   else
-    err = dispatch_gemv<0, uint16_t, uint16_t>(a, slots, s);
+    err = dispatch_gemv<0, uint16_t, uint16_t>(a, T, slots, s);
   if (err != hipSuccess) return err;
 
   // down
@@ -352,11 +356,11 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.K = L.I;
   a.N = L.d;
   if (L.act == MOE_F32)
-    err = dispatch_gemv<1, float, float>(a, slots, s);
+    err = dispatch_gemv<1, float, float>(a, T, slots, s);
   else if (L.wdt == MOE_I8)
-    err = dispatch_gemv<1, uint16_t, int8_t>(a, slots, s);
+    err = dispatch_gemv<1, uint16_t, int8_t>(a, T, slots, s);
   else
-    err = dispatch_gemv<1, uint16_t, uint16_t>(a, slots, s);
+    err = dispatch_gemv<1, uint16_t, uint16_t>(a, T, slots, s);
   return err;
 }
 
