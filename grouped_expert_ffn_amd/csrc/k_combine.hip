@@ -3,12 +3,15 @@
 // Every output element is owned by one thread, which reads the token's k routed rows
 // through inv_perm, then its shared-expert rows, then the residual, and sums them in fp32
 // in exactly that order before a single rounding.  Loads and stores are 16 bytes per lane,
-// so the kernel streams rows at HBM rate.
+// and each thread has its rows' loads in flight together rather than one round trip per row.
 #include "moe_internal.h"
 
 namespace moe {
 
 namespace {
+
+constexpr int kSlotBatch = 8;  // routed rows in flight per thread
+constexpr int kMaxShared = 8;  // the descriptor's limit on shared experts
 
 template <typename AT>
 __global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int S,
@@ -23,8 +26,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int S,
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  auto add = [&](const AT* src, float wt, bool scaled) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src);
+  auto add = [&](const uint4& v, float wt, bool scaled) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
     if (sizeof(AT) == 2) {
 #pragma unroll
@@ -41,12 +43,32 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int S,
       }
     }
   };
-  for (int j = 0; j < k; ++j) {
-    const int r = inv_perm[(size_t)t * k + j];
-    if (r >= 0) add(rows + (size_t)r * d + c, w[(size_t)t * k + j], true);  // < 0: dropped
+  auto load = [&](const AT* src) { return *reinterpret_cast<const uint4*>(src); };
+  // routed rows, eight slots at a time: the batch's loads are all in flight before the first
+  // is summed (a dropped slot, inv_perm < 0, reads row 0 and is skipped), then the sums run
+  // in slot order
+  for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+    uint4 v[kSlotBatch];
+    int r[kSlotBatch];
+#pragma unroll
+    for (int u = 0; u < kSlotBatch; ++u) {
+      r[u] = j0 + u < k ? inv_perm[(size_t)t * k + j0 + u] : -1;
+      v[u] = load(rows + (size_t)(r[u] < 0 ? 0 : r[u]) * d + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotBatch; ++u)
+      if (r[u] >= 0) add(v[u], w[(size_t)t * k + j0 + u], true);
   }
-  for (int s = 0; s < S; ++s) add(rows + ((size_t)T * k + (size_t)s * T + t) * d + c, 1.f, false);
-  if (residual) add(residual + (size_t)t * d + c, 1.f, false);
+  // shared-expert rows and the residual, loaded together, summed in that order
+  uint4 vs[kMaxShared + 1];
+#pragma unroll
+  for (int s = 0; s < kMaxShared; ++s)
+    if (s < S) vs[s] = load(rows + ((size_t)T * k + (size_t)s * T + t) * d + c);
+  if (residual) vs[kMaxShared] = load(residual + (size_t)t * d + c);
+#pragma unroll
+  for (int s = 0; s < kMaxShared; ++s)
+    if (s < S) add(vs[s], 1.f, false);
+  if (residual) add(vs[kMaxShared], 1.f, false);
   AT* dst = y + (size_t)t * d + c;
   if (sizeof(AT) == 2) {
     uint4 o;
