@@ -91,14 +91,11 @@ hipError_t launch_combine(const LayerDims& L, int T, const void* rows, const int
   const int V = L.act == MOE_F32 ? 4 : 8;
   const int per_block = 256 * V;
   dim3 grid(T, (L.d + per_block - 1) / per_block);
-  LaunchTimer timer(MOE_KERNEL_COMBINE, s);
   if (L.act == MOE_F32)
-    k_combine<float><<<grid, 256, 0, s>>>(T, L.d, L.k, L.S, (const float*)rows, inv_perm, topk_w,
-                                          (const float*)residual, (float*)y);
-  else
-    k_combine<uint16_t><<<grid, 256, 0, s>>>(T, L.d, L.k, L.S, (const uint16_t*)rows, inv_perm,
-                                             topk_w, (const uint16_t*)residual, (uint16_t*)y);
-  return hipGetLastError();
+    return launch(MOE_KERNEL_COMBINE, k_combine<float>, grid, 256, 0, s, T, L.d, L.k, L.S,
+                  (const float*)rows, inv_perm, topk_w, (const float*)residual, (float*)y);
+  return launch(MOE_KERNEL_COMBINE, k_combine<uint16_t>, grid, 256, 0, s, T, L.d, L.k, L.S,
+                (const uint16_t*)rows, inv_perm, topk_w, (const uint16_t*)residual, (uint16_t*)y);
 }
 
 }  // namespace moe

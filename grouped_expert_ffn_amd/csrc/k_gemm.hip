@@ -553,9 +553,8 @@ hipError_t run_ring(const GemmArgs& a, int grid, hipStream_t s) {
   static LdsFlags done;
   hipError_t e = set_lds(&k_gemm_ring<MODE, I8, TBN>, B::LDS, done);
   if (e != hipSuccess) return e;
-  LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-  k_gemm_ring<MODE, I8, TBN><<<grid, R_THREADS, B::LDS, s>>>(a);
-  return hipGetLastError();
+  return launch(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, k_gemm_ring<MODE, I8, TBN>, grid,
+                R_THREADS, B::LDS, s, a);
 }
 
 // tbn: N-tile width of the ring kernel (256 or 128), 0 for the general kernel
@@ -572,9 +571,8 @@ hipError_t run_gemm(GemmArgs a, int max_tiles, int tbn, hipStream_t s) {
   static LdsFlags done;
   hipError_t e = set_lds(&k_gemm<MODE, I8>, GEMM_LDS, done);
   if (e != hipSuccess) return e;
-  LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-  k_gemm<MODE, I8><<<grid, THREADS, GEMM_LDS, s>>>(a);
-  return hipGetLastError();
+  return launch(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, k_gemm<MODE, I8>, grid, THREADS,
+                GEMM_LDS, s, a);
 }
 
 // Tuned N-tile widths of the ring kernel.  A rule names one layer shape and the token ranges in

@@ -294,9 +294,8 @@ hipError_t run_gemv(GemvArgs a, int T, int slots, hipStream_t s) {
   a.mb_max = T < MB ? T : MB;  // no group holds more than T rows
   dim3 grid((a.N + 8 * CPG - 1) / (8 * CPG), slots);
   const size_t lds = (size_t)a.mb_max * ROUND * sizeof(AT);
-  LaunchTimer timer(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, s);
-  k_gemv<MODE, AT, WT, CPG, MAXIT, MB><<<grid, 256, lds, s>>>(a);
-  return hipGetLastError();
+  return launch(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, k_gemv<MODE, AT, WT, CPG, MAXIT, MB>,
+                grid, 256, lds, s, a);
 }
 
 // Pick MAXIT (K steps per wavefront) so one round covers K when possible, and CPG (channel

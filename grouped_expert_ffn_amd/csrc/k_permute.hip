@@ -306,14 +306,13 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
                           int tile_m, hipStream_t s) {
   const int N = T * L.k;
   int32_t* idsm = const_cast<int32_t*>(ids);
+  if (N <= kSingleMaxRows)
+    return launch(MOE_KERNEL_PERMUTE, k_permute<false>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m,
+                  nullptr, 0, nullptr, idsm, counts, offsets, perm, inv_perm, plan, nullptr,
+                  capacity_rows(L, T));
+  // two launches: the timer records its start before the first and its stop after the last
+  // launch made while it is alive
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
-  if (N <= kSingleMaxRows) {
-    k_permute<false><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
-                                        offsets, perm, inv_perm, plan, nullptr, capacity_rows(L, T));
-    return hipGetLastError();
-  }
-  // the timer brackets both launches: it records its start before the first and its stop
-  // after the last launch made while it is alive
   int32_t* chunk_hist = plan + plan_hist_offset(T, L.k, L.E, L.S);
   const int nb = (N + kPermChunk - 1) / kPermChunk;
   k_perm_hist<<<nb, 1024, 0, s>>>(N, L.E, ids, chunk_hist);
@@ -328,11 +327,9 @@ bool topk_permute_fusable(const LayerDims& L, int T) { return (size_t)T * L.k <=
 hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, int32_t* ids,
                                float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                                int32_t* inv_perm, int32_t* plan, int tile_m, hipStream_t s) {
-  LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
-  k_permute<true><<<1, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, logits, L.renorm, topk_w, ids,
-                                     counts, offsets, perm, inv_perm, plan, nullptr,
-                                     capacity_rows(L, T));
-  return hipGetLastError();
+  return launch(MOE_KERNEL_PERMUTE, k_permute<true>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m, logits,
+                L.renorm, topk_w, ids, counts, offsets, perm, inv_perm, plan, nullptr,
+                capacity_rows(L, T));
 }
 
 }  // namespace moe

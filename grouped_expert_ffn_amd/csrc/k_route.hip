@@ -283,24 +283,18 @@ hipError_t rmsnorm_typed(int T, int d, const AT* x, AT* y, float eps, hipStream_
   // the descriptor and pointer checks guarantee d % 16 == 0, d <= 16384 and aligned rows
   if (d % N != 0 || (((uintptr_t)x | (uintptr_t)y) & 15) != 0 || per_thread > 16)
     return hipErrorInvalidValue;
-  if (per_thread <= 1)
-    k_rmsnorm<AT, 1><<<T, 256, 0, s>>>(d, eps, x, y);
-  else if (per_thread <= 2)
-    k_rmsnorm<AT, 2><<<T, 256, 0, s>>>(d, eps, x, y);
-  else if (per_thread <= 4)
-    k_rmsnorm<AT, 4><<<T, 256, 0, s>>>(d, eps, x, y);
-  else if (per_thread <= 8)
-    k_rmsnorm<AT, 8><<<T, 256, 0, s>>>(d, eps, x, y);
-  else
-    k_rmsnorm<AT, 16><<<T, 256, 0, s>>>(d, eps, x, y);
-  return hipGetLastError();
+  const int id = MOE_KERNEL_RMSNORM;
+  if (per_thread <= 1) return launch(id, k_rmsnorm<AT, 1>, T, 256, 0, s, d, eps, x, y);
+  if (per_thread <= 2) return launch(id, k_rmsnorm<AT, 2>, T, 256, 0, s, d, eps, x, y);
+  if (per_thread <= 4) return launch(id, k_rmsnorm<AT, 4>, T, 256, 0, s, d, eps, x, y);
+  if (per_thread <= 8) return launch(id, k_rmsnorm<AT, 8>, T, 256, 0, s, d, eps, x, y);
+  return launch(id, k_rmsnorm<AT, 16>, T, 256, 0, s, d, eps, x, y);
 }
 
 }  // namespace
 
 hipError_t launch_rmsnorm(const LayerDims& L, int T, const void* x, void* xn, float eps,
                           hipStream_t s) {
-  LaunchTimer timer(MOE_KERNEL_RMSNORM, s);
   if (L.act == MOE_F32) return rmsnorm_typed<float>(T, L.d, (const float*)x, (float*)xn, eps, s);
   return rmsnorm_typed<uint16_t>(T, L.d, (const uint16_t*)x, (uint16_t*)xn, eps, s);
 }
@@ -316,10 +310,8 @@ hipError_t launch_router_logits(const LayerDims& L, int T, const void* x, const 
     // one 16-expert tile per block (four times the blocks of one block per token group, so
     // the router reads spread over more CUs)
     const dim3 grid((T + 15) / 16, (L.E + 15) / 16);
-    LaunchTimer timer(MOE_KERNEL_ROUTER, s);
-    k_router_mfma<1><<<grid, 512, 0, s>>>(T, L.d, L.E, (const uint16_t*)x, (const uint16_t*)w_router,
-                                          bias, logits);
-    return hipGetLastError();
+    return launch(MOE_KERNEL_ROUTER, k_router_mfma<1>, grid, 512, 0, s, T, L.d, L.E,
+                  (const uint16_t*)x, (const uint16_t*)w_router, bias, logits);
   }
   const int esz = L.act == MOE_F32 ? 4 : 2;
   int tb = kRouteTB;
@@ -328,21 +320,16 @@ hipError_t launch_router_logits(const LayerDims& L, int T, const void* x, const 
   const int epw = (T <= 64) ? 1 : (L.E + 3) / 4;
   dim3 grid((T + tb - 1) / tb, (L.E + 4 * epw - 1) / (4 * epw));
   const size_t lds = (size_t)tb * L.d * esz;
-  LaunchTimer timer(MOE_KERNEL_ROUTER, s);
   if (L.act == MOE_F32)
-    k_router_logits<float><<<grid, 256, lds, s>>>(T, L.d, L.E, epw, tb, (const float*)x,
-                                                  (const float*)w_router, bias, logits);
-  else
-    k_router_logits<uint16_t><<<grid, 256, lds, s>>>(T, L.d, L.E, epw, tb, (const uint16_t*)x,
-                                                     (const uint16_t*)w_router, bias, logits);
-  return hipGetLastError();
+    return launch(MOE_KERNEL_ROUTER, k_router_logits<float>, grid, 256, lds, s, T, L.d, L.E, epw, tb,
+                  (const float*)x, (const float*)w_router, bias, logits);
+  return launch(MOE_KERNEL_ROUTER, k_router_logits<uint16_t>, grid, 256, lds, s, T, L.d, L.E, epw,
+                tb, (const uint16_t*)x, (const uint16_t*)w_router, bias, logits);
 }
 
 hipError_t launch_topk(const LayerDims& L, int T, const float* logits, int32_t* ids, float* w,
                        hipStream_t s) {
-  LaunchTimer timer(MOE_KERNEL_TOPK, s);
-  k_topk<<<(T + 3) / 4, 256, 0, s>>>(T, L.E, L.k, L.renorm, logits, ids, w);
-  return hipGetLastError();
+  return launch(MOE_KERNEL_TOPK, k_topk, (T + 3) / 4, 256, 0, s, T, L.E, L.k, L.renorm, logits, ids, w);
 }
 
 }  // namespace moe

@@ -132,15 +132,25 @@ int32_t check_weights(const LayerDims& L, const moe_expert_weights_t* w) {
 
 }  // namespace
 
-LaunchTimer::LaunchTimer(int kernel, hipStream_t s) : stop_(nullptr), s_(s) {
+TimerEvents take_timer(int kernel) {
+  TimerEvents ev;
   if (kernel >= 0 && kernel < MOE_KERNEL_COUNT && g_timer_start[kernel]) {
-    (void)hipEventRecord((hipEvent_t)g_timer_start[kernel], s);
-    stop_ = g_timer_stop[kernel];
+    ev.start = (hipEvent_t)g_timer_start[kernel];
+    ev.stop = (hipEvent_t)g_timer_stop[kernel];
     g_timer_start[kernel] = g_timer_stop[kernel] = nullptr;
+  }
+  return ev;
+}
+
+LaunchTimer::LaunchTimer(int kernel, hipStream_t s) : stop_(nullptr), s_(s) {
+  const TimerEvents ev = take_timer(kernel);
+  if (ev.start) {
+    (void)hipEventRecord(ev.start, s);
+    stop_ = ev.stop;
   }
 }
 LaunchTimer::~LaunchTimer() {
-  if (stop_) (void)hipEventRecord((hipEvent_t)stop_, s_);
+  if (stop_) (void)hipEventRecord(stop_, s_);
 }
 
 constexpr int kGemvMaxTokens = 8;           // with shared experts

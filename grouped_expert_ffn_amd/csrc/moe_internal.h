@@ -2,6 +2,7 @@
 // Everything here is gfx950 (CDNA4, wave64) code; nothing is exported.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -129,12 +130,28 @@ inline size_t plan_words(int T, int k, int E, int S) {
 // launchers (each returns hipSuccess or the launch error)
 // -------------------------------------------------------------------------------------
 // Brackets one kernel launch with the caller's events when moe_time_next_launch armed it.
+// Timing hook (moe_time_next_launch).  A step that is one launch goes through launch(): the
+// armed events are handed to the launch itself (hipExtLaunchKernelGGL records them from the
+// dispatch, i.e. the kernel's own start and end).  A step of several launches is bracketed
+// by a LaunchTimer, which records the events on the stream around them.
+struct TimerEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+TimerEvents take_timer(int kernel);  // the events armed for `kernel` (then disarmed), or nulls
+
+template <typename F, typename... Args>
+hipError_t launch(int kernel, F f, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+  const TimerEvents ev = take_timer(kernel);
+  hipExtLaunchKernelGGL(f, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+  return hipGetLastError();
+}
+
 class LaunchTimer {
  public:
   LaunchTimer(int kernel, hipStream_t s);
   ~LaunchTimer();
  private:
-  void* stop_;
+  hipEvent_t stop_;
   hipStream_t s_;
 };
 

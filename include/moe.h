@@ -185,9 +185,11 @@ typedef enum {
 } moe_kernel_t;
 
 /* One-shot timing hook for measuring a single kernel inside a call: the next launch of
- * `kernel` made by this thread (through any entry point) is bracketed by
- * hipEventRecord(start_event) and hipEventRecord(stop_event) on that launch's stream, and
- * the hook is then cleared.  The events (hipEvent_t) are created and owned by the caller;
+ * `kernel` made by this thread (through any entry point) records start_event and stop_event
+ * on that launch's stream, and the hook is then cleared.  A step that is one launch hands
+ * the events to the launch itself (hipExtLaunchKernel), so they hold the kernel's own start
+ * and end, the window a profiler's kernel trace reports; the multi-workgroup sort (two
+ * launches) is bracketed by hipEventRecord before the first and after the second.  The events (hipEvent_t) are created and owned by the caller;
  * NULL events disarm the hook.  Returns MOE_ERR_INVALID for an unknown kernel. */
 int32_t moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event);
 
