@@ -50,14 +50,21 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int S,
   for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
     uint4 v[kSlotBatch];
     int r[kSlotBatch];
+    float wt[kSlotBatch];
+    // the batch's row indices and weights (whole batches as unconditional loads, which the
+    // compiler merges into wide scalar loads)
+    const bool full = j0 + kSlotBatch <= k;
 #pragma unroll
     for (int u = 0; u < kSlotBatch; ++u) {
-      r[u] = j0 + u < k ? inv_perm[(size_t)t * k + j0 + u] : -1;
-      v[u] = load(rows + (size_t)(r[u] < 0 ? 0 : r[u]) * d + c);
+      const size_t i = (size_t)t * k + (full ? j0 + u : min(j0 + u, k - 1));
+      r[u] = (full || j0 + u < k) ? inv_perm[i] : -1;
+      wt[u] = w[i];
     }
 #pragma unroll
+    for (int u = 0; u < kSlotBatch; ++u) v[u] = load(rows + (size_t)(r[u] < 0 ? 0 : r[u]) * d + c);
+#pragma unroll
     for (int u = 0; u < kSlotBatch; ++u)
-      if (r[u] >= 0) add(v[u], w[(size_t)t * k + j0 + u], true);
+      if (r[u] >= 0) add(v[u], wt[u], true);
   }
   // shared-expert rows and the residual, loaded together, summed in that order
   uint4 vs[kMaxShared + 1];

@@ -68,6 +68,8 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
     }
   };
   load_slice(e0, 0);  // in flight while the activations are staged
+  // the first expert's bias, fetched now rather than after the dot products
+  float b_next = (bias && e0 < E) ? bias[e0] : 0.f;
 
   // token rows -> LDS, eight loads per thread in flight before their stores
   uint4* xs = reinterpret_cast<uint4*>(smem);
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
       }
     }
     if (ei + 1 < epw && e + 1 < E) load_slice(e + 1, 0);  // next expert's row
-    const float b = bias ? bias[e] : 0.f;
+    const float b = b_next;
+    if (bias && ei + 1 < epw && e + 1 < E) b_next = bias[e + 1];
 #pragma unroll
     for (int t = 0; t < kRouteTB; ++t) {
       if (t < tb) {
