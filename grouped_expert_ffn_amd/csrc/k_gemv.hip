@@ -299,9 +299,11 @@ hipError_t run_gemv(GemvArgs a, int T, int slots, hipStream_t s) {
 }
 
 // Pick MAXIT (K steps per wavefront) so one round covers K when possible, and CPG (channel
-// groups per block).  Measured on the OLMoE shapes: more, smaller blocks beat fewer blocks
-// with more loads per lane once a block's loads fill a round trip, so the down projection
-// uses 2 channel groups and int8 gate/up 1 (a lane's 16 bytes hold twice the weights).  Rows
+// groups per block).  Measured on the OLMoE and DeepSeek shapes: more, smaller blocks beat
+// fewer blocks with more loads per lane once a block's loads fill a round trip, so the down
+// projection and int8 gate/up (a lane's 16 bytes hold twice the weights) use 1 channel
+// group when a wavefront covers K in 4-8 steps (down at CPG 1 against 2: -4% at OLMoE T=8,
+// -8% at DeepSeek T=8).  Rows
 // go in chunks of 4 when one round covers K (the registers saved raise the occupancy the
 // bandwidth follows), else of 8 (each further chunk would read the weights again).
 template <int MODE, typename AT, typename WT>
@@ -311,8 +313,8 @@ hipError_t dispatch_gemv(const GemvArgs& a, int T, int slots, hipStream_t s) {
   const int steps = (a.K + 8 * V - 1) / (8 * V);
   const int spw = (steps + kWaves - 1) / kWaves;
   if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 2), 2, 4>(a, T, slots, s);
-  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 2 && V == 16 ? 1 : 2), 4, 4>(a, T, slots, s);
-  if (spw <= 8) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8, 4>(a, T, slots, s);
+  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 1 || V == 16 ? 1 : 2), 4, 4>(a, T, slots, s);
+  if (spw <= 8) return run_gemv<MODE, AT, WT, 1, 8, 4>(a, T, slots, s);
   return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8, 8>(a, T, slots, s);
 }
 
