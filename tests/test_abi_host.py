@@ -141,3 +141,14 @@ def test_zero_tokens_is_a_no_op(L):
     abi.moe_forward(d, 0, 0x1000, 0x1000, None, w, None, 0x1000, None, None, 0x1000, 1 << 20,
                     stream=0)
     assert abi.last_error() == ""
+
+
+def test_timing_hook_refusals(L):
+    # host-only argument checks of moe_time_next_launch (no events are touched)
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moe_time_next_launch(-1, None, None) == abi.MOE_ERR_INVALID
+    assert L.moe_time_next_launch(abi.MOE_KERNEL_COMBINE + 1, None, None) == abi.MOE_ERR_INVALID
+    assert L.moe_time_next_launch(abi.MOE_KERNEL_GATE_UP, fake, None) == abi.MOE_ERR_INVALID
+    assert L.moe_time_next_launch(abi.MOE_KERNEL_GATE_UP, None, fake) == abi.MOE_ERR_INVALID
+    # both NULL disarms, which is always valid
+    assert L.moe_time_next_launch(abi.MOE_KERNEL_GATE_UP, None, None) == abi.MOE_OK
