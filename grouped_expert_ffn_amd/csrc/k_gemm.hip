@@ -52,7 +52,7 @@ constexpr size_t GEMM_LDS = 2 * STAGE_ELEMS * sizeof(uint16_t);
 
 // ring kernel
 constexpr int RBK = 32;  // K elements per stage
-constexpr int RNST = 3;  // stages in the ring (two workgroups per CU fit in LDS)
+constexpr int kRing128 = 3;  // ring depth of the 128-wide tile (the 256-wide one: 3)
 
 struct GemmArgs {
   const void* in;   // gate/up: x [T, K] (gathered through perm); down: h [R, K]
@@ -306,8 +306,23 @@ __global__ __launch_bounds__(THREADS) void k_gemm(const GemmArgs a) {
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));  // vmcnt bits [3:0] and [15:14]
+}
+// wait until at most `ahead` stages of LPS loads each (0 <= ahead <= MAXA) are still pending
+template <int LPS, int MAXA>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (MAXA >= 4) {
+    if (ahead >= 4) return wait_vmcnt<4 * LPS>();
+  }
+  if constexpr (MAXA >= 3) {
+    if (ahead == 3) return wait_vmcnt<3 * LPS>();
+  }
+  if constexpr (MAXA >= 2) {
+    if (ahead == 2) return wait_vmcnt<2 * LPS>();
+  }
+  if (ahead == 1) return wait_vmcnt<LPS>();
+  wait_vmcnt<0>();
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -315,7 +330,8 @@ typedef const __attribute__((address_space(1))) void global_void;
 
 // Tile RBM x TBN (gate/up: TBN/2 gate + the same TBN/2 up channels), TBN = 256 or 128; four
 // wavefronts side by side, each owning all RBM rows and TBN/4 columns (gate/up: TBN/8 gate +
-// the same up channels); K advances RBK=32 per stage through an RNST-deep ring.
+// the same up channels); K advances RBK=32 per stage through an NST-deep ring (two
+// workgroups per CU fit in LDS).
 constexpr int RBM = 128, RWN = 4;
 constexpr int R_THREADS = 64 * RWN;
 constexpr int R_TI = RBM / 16;  // 16-row MFMA slices per tile
@@ -333,12 +349,13 @@ struct RingB {
   static constexpr int RPI = 64 / LPR;                     // B rows per DMA load
   static constexpr int DMA = TBN / RPI / RWN;              // B loads per stage per wavefront
   static constexpr int LPS = R_DMA_A + DMA;                // loads per stage per wavefront
-  static constexpr size_t LDS = (size_t)RNST * STAGE;
+  static constexpr int NST = TBN == 128 ? kRing128 : 3;    // stages in the ring
+  static constexpr size_t LDS = (size_t)NST * STAGE;
   // waves per SIMD the registers are sized for: 2 with 32 accumulator tiles per wavefront,
   // 3 with 16 when the LDS holds three workgroups per CU (160 KiB)
   static constexpr int WAVES_PER_EU = (TJ == 2 && 160 * 1024 / LDS >= 3) ? 3 : 2;
   static_assert(DMA * RPI * RWN == TBN && TJ % 2 == 0, "tile split");
-  static_assert((RNST - 2) * LPS < 16, "vmcnt range");
+  static_assert((NST - 2) * LPS < 64 && NST >= 3 && NST <= 6, "vmcnt range");
 };
 
 // 8 int8 weights -> 8 bf16 (exact for |q| <= 127)
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     b_src[i] = b_row_t<MODE, TBN>(a, w, row, W8 ? 1 : 2);
   }
   auto issue = [&](int kt) {
-    unsigned char* st = rlds + (kt % RNST) * B::STAGE;
+    unsigned char* st = rlds + (kt % B::NST) * B::STAGE;
     const int kb = kt * RBK;
 #pragma unroll
     for (int i = 0; i < R_DMA_A; ++i)
@@ -434,26 +451,21 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
 
   const int nk = K / RBK;
 #pragma unroll
-  for (int s = 0; s < RNST - 1; ++s)
+  for (int s = 0; s < B::NST - 1; ++s)
     if (s < nk) issue(s);
   // the K loop, instantiated per number of live 16-row slices so that it has no branches
   auto k_loop = [&](auto live) {
     constexpr int NI = decltype(live)::value;
     for (int kt = 0; kt < nk; ++kt) {
       // stage kt is complete once at most (stages issued after it) * B::LPS loads are pending
-      const int ahead = min(nk - 1, kt + RNST - 2) - kt;
-      if (ahead >= 2)
-        wait_vmcnt<2 * B::LPS>();
-      else if (ahead == 1)
-        wait_vmcnt<B::LPS>();
-      else
-        wait_vmcnt<0>();
+      const int ahead = min(nk - 1, kt + B::NST - 2) - kt;
+      wait_ahead<B::LPS, B::NST - 2>(ahead);
       // Every wavefront waited for its own loads of stage kt above, so after this barrier the
       // whole stage is in LDS and every wavefront is done with stage kt-1.  A plain
       // s_barrier: __syncthreads() would add a release fence, i.e. wait for all loads in flight.
       asm volatile("s_barrier" ::: "memory");
-      if (kt + RNST - 1 < nk) issue(kt + RNST - 1);
-      const unsigned char* st = rlds + (kt % RNST) * B::STAGE;
+      if (kt + B::NST - 1 < nk) issue(kt + B::NST - 1);
+      const unsigned char* st = rlds + (kt % B::NST) * B::STAGE;
       bf16x8 bfr[R_TJ], af[NI];
 #pragma unroll
       for (int j = 0; j < R_TJ; ++j)
