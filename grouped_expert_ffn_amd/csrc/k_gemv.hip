@@ -305,7 +305,8 @@ hipError_t run_gemv(GemvArgs a, int T, int slots, hipStream_t s) {
 // group when a wavefront covers K in 4-8 steps (down at CPG 1 against 2: -4% at OLMoE T=8,
 // -8% at DeepSeek T=8).  Rows
 // go in chunks of 4 when one round covers K (the registers saved raise the occupancy the
-// bandwidth follows), else of 8 (each further chunk would read the weights again).
+// bandwidth follows; at T = 1 and 2 chunks of T, 2-4% faster still), else of 8 (each
+// further chunk would read the weights again).
 template <int MODE, typename AT, typename WT>
 hipError_t dispatch_gemv(const GemvArgs& a, int T, int slots, hipStream_t s) {
   constexpr int V = WTraits<WT>::V;
@@ -313,8 +314,17 @@ hipError_t dispatch_gemv(const GemvArgs& a, int T, int slots, hipStream_t s) {
   const int steps = (a.K + 8 * V - 1) / (8 * V);
   const int spw = (steps + kWaves - 1) / kWaves;
   if (spw <= 2) return run_gemv<MODE, AT, WT, (NMAT == 2 ? 4 : 2), 2, 4>(a, T, slots, s);
-  if (spw <= 4) return run_gemv<MODE, AT, WT, (NMAT == 1 || V == 16 ? 1 : 2), 4, 4>(a, T, slots, s);
-  if (spw <= 8) return run_gemv<MODE, AT, WT, 1, 8, 4>(a, T, slots, s);
+  if (spw <= 4) {
+    constexpr int C = NMAT == 1 || V == 16 ? 1 : 2;
+    if (T == 1) return run_gemv<MODE, AT, WT, C, 4, 1>(a, T, slots, s);
+    if (T == 2) return run_gemv<MODE, AT, WT, C, 4, 2>(a, T, slots, s);
+    return run_gemv<MODE, AT, WT, C, 4, 4>(a, T, slots, s);
+  }
+  if (spw <= 8) {
+    if (T == 1) return run_gemv<MODE, AT, WT, 1, 8, 1>(a, T, slots, s);
+    if (T == 2) return run_gemv<MODE, AT, WT, 1, 8, 2>(a, T, slots, s);
+    return run_gemv<MODE, AT, WT, 1, 8, 4>(a, T, slots, s);
+  }
   return run_gemv<MODE, AT, WT, (NMAT == 2 ? 1 : 2), 8, 8>(a, T, slots, s);
 }
 
