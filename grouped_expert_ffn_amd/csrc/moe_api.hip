@@ -158,11 +158,11 @@ constexpr int kGemvMaxTokensRouted = 16;    // routed experts only
 
 int ffn_tile_m(const LayerDims& L, int T) {
   if (L.act == MOE_F32) return 0;
-  // The GEMV streams each group's weights once and does its rows in passes of up to 8.
+  // The GEMV streams each group's weights once and does its rows in passes of a few rows.
   // A shared expert holds all T rows, so past 8 tokens it needs several passes and the
-  // matrix-core GEMM is faster (measured at T = 16 and 32 on the DeepSeek shapes); with
-  // routed experts only, groups stay small enough for the GEMV up to 16 tokens (measured
-  // at T = 9, 12 and 16 on the OLMoE shapes).
+  // matrix-core GEMM is as fast or faster (DeepSeek shapes: equal layer time at T = 9 and
+  // 12, 15% faster at 16); with routed experts only, groups stay small enough for the GEMV
+  // up to 16 tokens (measured at T = 9, 12 and 16 on the OLMoE shapes).
   const int gemv_max = L.S > 0 ? kGemvMaxTokens : kGemvMaxTokensRouted;
   return T > gemv_max ? gemm_tile_m(L) : 0;
 }
