@@ -189,6 +189,8 @@ SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     (S.DEEPSEEK_I8, 512),
     # the tuned tile widths: gate/up 128 + down 256, gate/up 256 + down 128 (bf16 and int8)
     (S.DEEPSEEK_BF16, 40), (S.DEEPSEEK_BF16, 450), (S.DEEPSEEK_I8, 24), (S.DEEPSEEK_I8, 100),
+    # the GEMV at its largest sizes (routed experts only: groups of several 4-row chunks)
+    (S.OLMOE_BF16, 32), (S.OLMOE_I8, 16),
 ]
 
 
