@@ -626,7 +626,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
                           "(the path has no multi-GPU sharding or collectives)"}), flush=True)
         sys.exit(2)
     import torch

@@ -33,7 +33,7 @@ What the layer computes, from the pages:
   (the same section, "What dropping tokens costs": capacity factors 2.0 and
   1.0 against dropless).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 softmax over all E logits, then top-k, then optional renormalisation; the
 selection is made on the logits (softmax is strictly increasing, so this is
 the same set), largest first, equal logits going to the lower expert id, NaN
