@@ -1,11 +1,13 @@
 // Top-k gating of one token by one wavefront; shared by the top-k and fused permute kernels.
 //
 // Lane l holds the logits of experts l, l+64, l+128 and l+192 (E <= 256), each with an
-// order-preserving 32-bit code (NaN lowest).  The k slots are filled in k rounds: every lane
-// offers its best remaining expert (highest code, then lowest id), a wave-wide max over the
-// offers picks the code, a wave-wide min over the lanes offering that code picks the lowest
-// id, and that expert leaves the pool.  Slots are therefore ordered by descending logit,
-// equal logits go to the lower expert id, and NaN ranks below every number.
+// order-preserving 32-bit code (NaN lowest).  Up to 64 experts the wavefront sorts the keys
+// (code, 255 - expert) with a 21-step bitonic network and lane r holds slot r.  Beyond, the
+// k slots are filled in k rounds: every lane offers its best remaining expert (highest code,
+// then lowest id), a wave-wide max over the offers picks the code, a wave-wide min over the
+// lanes offering that code picks the lowest id, and that expert leaves the pool.  Either way
+// slots are ordered by descending logit, equal logits go to the lower expert id, and NaN
+// ranks below every number.
 #pragma once
 
 #include "moe_internal.h"
@@ -54,12 +56,97 @@ __device__ __forceinline__ void topk_load(const float* __restrict__ lrow, int E,
   }
 }
 
+// inverse of order_bits (NaN comes back as a NaN, -0 as +0)
+__device__ __forceinline__ float from_order_bits(uint32_t c) {
+  return __uint_as_float((c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
+// the value of lane ^ STRIDE (STRIDE a power of two below 64)
+template <int STRIDE>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (STRIDE == 1) {
+    return dpp_u<0xB1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (STRIDE == 2) {
+    return dpp_u<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (STRIDE < 32) {
+    // ds_swizzle bit mode within 32 lanes: and-mask 0x1F, or-mask 0, xor-mask STRIDE
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (STRIDE << 10));
+  } else {
+    return (uint32_t)__shfl_xor((int)v, 32, kWave);
+  }
+}
+
+// one compare-exchange of a bitonic network over the wavefront (blocks of SIZE lanes, pairs
+// STRIDE apart): the lane keeps the larger key where the final order is descending
+template <int STRIDE, int SIZE>
+__device__ __forceinline__ uint64_t bitonic_cx(uint64_t key, int lane) {
+  const uint64_t other = ((uint64_t)xor_lane<STRIDE>((uint32_t)(key >> 32)) << 32) |
+                         xor_lane<STRIDE>((uint32_t)key);
+  const bool keep_max = ((lane & SIZE) == 0) == ((lane & STRIDE) == 0);
+  return keep_max == (key > other) ? key : other;
+}
+
+// the lanes' 64-bit keys sorted in descending order, lane 0 holding the largest
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {
+  key = bitonic_cx<1, 2>(key, lane);
+  key = bitonic_cx<2, 4>(key, lane);
+  key = bitonic_cx<1, 4>(key, lane);
+  key = bitonic_cx<4, 8>(key, lane);
+  key = bitonic_cx<2, 8>(key, lane);
+  key = bitonic_cx<1, 8>(key, lane);
+  key = bitonic_cx<8, 16>(key, lane);
+  key = bitonic_cx<4, 16>(key, lane);
+  key = bitonic_cx<2, 16>(key, lane);
+  key = bitonic_cx<1, 16>(key, lane);
+  key = bitonic_cx<16, 32>(key, lane);
+  key = bitonic_cx<8, 32>(key, lane);
+  key = bitonic_cx<4, 32>(key, lane);
+  key = bitonic_cx<2, 32>(key, lane);
+  key = bitonic_cx<1, 32>(key, lane);
+  key = bitonic_cx<32, 64>(key, lane);
+  key = bitonic_cx<16, 64>(key, lane);
+  key = bitonic_cx<8, 64>(key, lane);
+  key = bitonic_cx<4, 64>(key, lane);
+  key = bitonic_cx<2, 64>(key, lane);
+  key = bitonic_cx<1, 64>(key, lane);
+  return key;
+}
+
+// Top-k for E <= 64 (one logit per lane), with the same result as the k rounds below: the
+// keys (code, 255 - expert) are sorted across the wavefront, so lane r holds slot r
+// (descending logit, the lower expert first among equal codes, NaN last); a lane's expert is
+// chosen when its key is at least the k-th largest.  The softmax sums run over the same
+// lanes in the same order as below, and a slot's weight is recomputed from its exactly
+// recovered logit, so the outputs are identical.
+__device__ __forceinline__ void topk_select_wave(const float (&l)[4], int E, int k, int renorm,
+                                                 int lane, int32_t* __restrict__ ids,
+                                                 float* __restrict__ wout, int t, int* keys_lds) {
+  const bool valid = lane < E;
+  const uint64_t key =
+      valid ? (((uint64_t)order_bits(l[0]) << 32) | (uint32_t)(255 - lane)) : 0ull;
+  const uint64_t top = wave_sort_desc(key, lane);
+  const uint64_t kth = ((uint64_t)readlane_u((uint32_t)(top >> 32), k - 1) << 32) |
+                       readlane_u((uint32_t)top, k - 1);
+  const float m = wave_max_u(fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+  const float z = valid ? expf(l[0] - m) : 0.f;
+  const float zsum = wave_sum_u(z);
+  const float den = renorm ? wave_sum_u((valid && key >= kth) ? z : 0.f) : zsum;
+  if (lane < k) {
+    const int e = 255 - (int)(uint32_t)top;
+    const float zt = expf(from_order_bits((uint32_t)(top >> 32)) - m);
+    ids[(size_t)t * k + lane] = e;
+    wout[(size_t)t * k + lane] = zt / den;
+    if (keys_lds) keys_lds[t * k + lane] = e;
+  }
+}
+
 // Top-k gating of token t from its loaded logits, by one whole wavefront (all 64 lanes
 // active).  Writes ids/w of the token's k slots; when keys_lds is given, the ids are also
 // written there at t*k + slot.
 __device__ __forceinline__ void topk_select(const float (&l)[4], int E, int k, int renorm, int lane,
                                             int32_t* __restrict__ ids, float* __restrict__ wout, int t,
                                             int* keys_lds) {
+  if (E <= kWave) return topk_select_wave(l, E, k, renorm, lane, ids, wout, t, keys_lds);
   const int slots = (E + kWave - 1) / kWave;
   uint32_t code[4];
   bool live[4];
