@@ -98,13 +98,26 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
     for (int t = 0; t < kRouteTB; ++t) acc[t] = 0.f;
     for (int c0 = 0; c0 < row_chunks; c0 += kWave * R) {
       if (c0 > 0) load_slice(e, c0);
+      // A step whose 64 chunks all lie in the row has no per-lane test, so its LDS reads are
+      // issued together; token rows past this block's are clamped into the staged rows (their
+      // sums are never stored).  Only a partial last step tests each lane.
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int c = c0 + lane + kWave * i;
-        if (c < row_chunks) {
+        const int cb = c0 + kWave * i;
+        if (cb >= row_chunks) break;
+        const int c = cb + lane;
+        if (cb + kWave <= row_chunks) {
 #pragma unroll
-          for (int t = 0; t < kRouteTB; ++t)
-            if (t < tb) acc[t] += dot_chunk<AT>(wv[i], xs[t * row_chunks + c]);
+          for (int t = 0; t < kRouteTB; ++t) {
+            const int tr = t < tb ? t : tb - 1;
+            acc[t] += dot_chunk<AT>(wv[i], xs[tr * row_chunks + c]);
+          }
+        } else if (c < row_chunks) {
+#pragma unroll
+          for (int t = 0; t < kRouteTB; ++t) {
+            const int tr = t < tb ? t : tb - 1;
+            acc[t] += dot_chunk<AT>(wv[i], xs[tr * row_chunks + c]);
+          }
         }
       }
     }
