@@ -124,13 +124,28 @@ __global__ __launch_bounds__(256) void k_router_logits(int T, int d, int E, int 
     if (ei + 1 < epw && e + 1 < E) load_slice(e + 1, 0);  // next expert's row
     const float b = b_next;
     if (bias && ei + 1 < epw && e + 1 < E) b_next = bias[e + 1];
+    // the 8 token sums over the wavefront, halving the values each lane carries: lanes
+    // exchange half of them at strides 32, 16 and 8 (then lane l carries token (l >> 3) & 7),
+    // and the remaining single value is summed at strides 4, 2 and 1 (fixed order)
+    static_assert(kRouteTB == 8, "butterfly over 8 token sums");
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    float v4[4], v2[2];
 #pragma unroll
-    for (int t = 0; t < kRouteTB; ++t) {
-      if (t < tb) {
-        const float sum = wave_sum_u(acc[t]);
-        if (lane == 0) logits[(size_t)(t0 + t) * E + e] = sum + b;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float mine = h5 ? acc[j + 4] : acc[j], give = h5 ? acc[j] : acc[j + 4];
+      v4[j] = mine + __uint_as_float(xor_lane<32>(__float_as_uint(give)));
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float mine = h4 ? v4[j + 2] : v4[j], give = h4 ? v4[j] : v4[j + 2];
+      v2[j] = mine + __uint_as_float(xor_lane<16>(__float_as_uint(give)));
+    }
+    float tot = (h3 ? v2[1] : v2[0]) + __uint_as_float(xor_lane<8>(__float_as_uint(h3 ? v2[0] : v2[1])));
+    tot += __uint_as_float(xor_lane<4>(__float_as_uint(tot)));
+    tot += __uint_as_float(xor_lane<2>(__float_as_uint(tot)));
+    tot += __uint_as_float(xor_lane<1>(__float_as_uint(tot)));
+    const int t = lane >> 3;
+    if ((lane & 7) == 0 && t < tb) logits[(size_t)(t0 + t) * E + e] = tot + b;
   }
 }
 
