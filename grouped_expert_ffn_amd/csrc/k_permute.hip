@@ -40,6 +40,20 @@ constexpr int kStageLoads = kSingleMaxRows / (kPermWaves * kWave);  // staging l
 static_assert(kFusedMaxRows <= kSingleMaxRows, "the fused kernel sorts in one workgroup");
 static_assert(kPermChunk == kPermWaves * kWave, "one 64-row step per wavefront and chunk");
 
+// Inclusive prefix sum over the wavefront's 64 lanes (all active): a Hillis-Steele scan
+// inside each row of 16 lanes by DPP row shifts (a lane with no source lane adds 0), then
+// each row adds the totals of the rows before it, read from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+}
+
 __device__ __forceinline__ uint64_t peer_mask(int key, bool valid) {
   uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -164,15 +178,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
       s += c[i];
       sf += c[i] > 0;
     }
-    int incl = s, inclf = sf;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off, kWave), of = __shfl_up(inclf, off, kWave);
-      if (lane >= off) {
-        incl += o;
-        inclf += of;
-      }
-    }
+    const int incl = wave_incl_scan(s, lane), inclf = wave_incl_scan(sf, lane);
     int ex = incl - s, exf = inclf - sf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -239,12 +245,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
         nt[i] = (rows + tile_m - 1) / tile_m;
         s += nt[i];
       }
-      int incl = s;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-      }
+      const int incl = wave_incl_scan(s, lane);
       int ex = incl - s;
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
