@@ -45,10 +45,12 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 
-DEFAULT_SWEEP = ("olmoe_bf16:1,olmoe_bf16:2,olmoe_bf16:4,olmoe_bf16:9,olmoe_bf16:64,"
-                 "olmoe_i8:1,olmoe_i8:8,olmoe_i8:64,olmoe_i8_zipf:8,"
-                 "deepseek_bf16:1,deepseek_bf16:16,deepseek_bf16:128,deepseek_bf16:512,"
-                 "deepseek_bf16:2048")
+# the curve over T = 1, 2, 4, ..., 2048 on the OLMoE-shaped (uniform) and DeepSeek-shaped
+# (Zipf) layers, the speculative-verify size T = 9, and the int8 points
+_POW2 = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048)
+DEFAULT_SWEEP = ",".join([f"olmoe_bf16:{t}" for t in sorted(set(_POW2) - {8} | {9})] +
+                         ["olmoe_i8:1", "olmoe_i8:8", "olmoe_i8:64", "olmoe_i8_zipf:8"] +
+                         [f"deepseek_bf16:{t}" for t in _POW2])
 
 
 def parse():
