@@ -27,6 +27,11 @@
 //    applied on the source side (each lane fetches a permuted 16-byte piece of its row).
 //    int8 weights are widened to bf16 (exact) as they are read from LDS, and the
 //    per-channel scales multiply the fp32 sums in the epilogue.
+//  * k_gemm_ring64 (bf16 weights, K a multiple of 64): the ring kernel's tiles, wavefronts
+//    and epilogue, with the weights staged 64 K deep (128 bytes, a whole cache line, of each
+//    row per block, so a DMA instruction covers 8 full lines instead of 16 half lines) in two
+//    slots, and the activations 32 K deep in two slots.  Used for bf16 weights whenever K
+//    allows; k_gemm_ring serves int8 weights and K % 64 == 32.
 //  * k_gemm (any K that is a multiple of 16): 128x128 tiles, four wavefronts in a 2x2 layout
 //    each owning 64x64.  BK=64, LDS double buffer (rows padded by 16 bytes) with a register
 //    prefetch of the next K-step; int8 weights are widened to bf16 on the way into LDS.
@@ -536,6 +541,179 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// ring kernel with full-line weight blocks (bf16 weights, K % 64 == 0)
+// ------------------------------------------------------------------------------------------
+// The same tile, wavefront layout, operand order and epilogue as k_gemm_ring, with the LDS
+// split into two 8 KiB activation slots (32 K per step) and two weight slots of 64 K per
+// block: 128 bytes of each weight row, one whole cache line, so one weight DMA instruction
+// covers 8 rows x 128 bytes instead of 16 rows x 64 bytes (half as many cache lines per
+// byte, which is what the weight path of the 32-deep ring pays for).  A weight block is
+// issued one block (two steps) ahead of its use, an activation step one step ahead.
+template <int TBN>
+struct Ring64 {
+  static constexpr int TJ = TBN / RWN / 16;            // 16-column MFMA tiles per wavefront
+  static constexpr int A_SLOT = R_A_BYTES;              // 128 rows x 64 bytes
+  static constexpr int B_SLOT = TBN * 128;              // TBN rows x 128 bytes
+  static constexpr int LDS = 2 * A_SLOT + 2 * B_SLOT;   // 80 KiB (256) / 48 KiB (128)
+  static constexpr int DMA_B = TBN / 8 / RWN;           // weight loads per block per wavefront
+  static constexpr int WAVES_PER_EU = 160 * 1024 / LDS >= 3 ? 3 : 2;
+  static_assert(DMA_B * 8 * RWN == TBN && TJ % 2 == 0, "tile split");
+};
+
+template <int MODE, int TBN>
+__global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
+    Ring64<TBN>::WAVES_PER_EU))) void k_gemm_ring64(const GemmArgs a) {
+  using B = Ring64<TBN>;
+  constexpr int R_TJ = B::TJ;
+  extern __shared__ __align__(16) unsigned char rlds[];
+  Work w;
+  if (!map_work_t<RBM>(a, w)) return;
+  const int K = a.K;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+  // Activation DMA as in k_gemm_ring: load q = wave*R_DMA_A + i fills rows 16q .. 16q+15,
+  // lane l row 16q + l/4, 16-byte position l%4 with the row's chunk (l%4) ^ ((row >> 2) & 3).
+  // Weight DMA: load q = wave*DMA_B + i fills rows 8q .. 8q+7, lane l row 8q + l/8, 16-byte
+  // position l%8 with the row's chunk (l%8) ^ swzb(row), swzb(row) = (row >> 1) & 7, which
+  // keeps the 16 rows an MFMA operand read touches on distinct banks.
+  const uint16_t* a_src[R_DMA_A];
+  int ca[R_DMA_A];
+#pragma unroll
+  for (int i = 0; i < R_DMA_A; ++i) {
+    const int row = 16 * (wave * R_DMA_A + i) + lane / 4;
+    ca[i] = ((lane % 4) ^ ((row >> 2) & 3)) * 8;
+    a_src[i] = a_row_t<MODE>(a, w, w.m0 + row);
+  }
+  const unsigned char* b_src[B::DMA_B];
+#pragma unroll
+  for (int i = 0; i < B::DMA_B; ++i) {
+    const int row = 8 * (wave * B::DMA_B + i) + lane / 8;
+    b_src[i] = b_row_t<MODE, TBN>(a, w, row, 2) + ((lane % 8) ^ ((row >> 1) & 7)) * 16;
+  }
+  auto issue_a = [&](int kt) {  // step kt (32 K) into activation slot kt % 2
+    unsigned char* st = rlds + (kt & 1) * B::A_SLOT;
+#pragma unroll
+    for (int i = 0; i < R_DMA_A; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(a_src[i] + kt * RBK + ca[i]),
+                                       (lds_void*)(st + (wave * R_DMA_A + i) * 1024), 16, 0, 0);
+  };
+  auto issue_b = [&](int jb) {  // block jb (64 K) into weight slot jb % 2
+    unsigned char* st = rlds + 2 * B::A_SLOT + (jb & 1) * B::B_SLOT;
+#pragma unroll
+    for (int i = 0; i < B::DMA_B; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(b_src[i] + jb * 128),
+                                       (lds_void*)(st + (wave * B::DMA_B + i) * 1024), 16, 0, 0);
+  };
+
+  const int wn = wave, lr = lane % 16;
+  const int rd_chunk = ((lane / 16) ^ ((lr >> 2) & 3)) * 16;
+  int a_off[R_TI];
+#pragma unroll
+  for (int i = 0; i < R_TI; ++i) a_off[i] = (i * 16 + lr) * 64 + rd_chunk;
+  // weight operand of tile j in half h of a block: row r, logical chunk 4h + lane/16
+  int b_off[2][R_TJ];
+#pragma unroll
+  for (int j = 0; j < R_TJ; ++j) {
+    int row;
+    if (MODE == 0)  // first half of the tiles: gate channels, second half: the same up channels
+      row = (j < R_TJ / 2 ? 0 : TBN / 2) + wn * (TBN / RWN / 2) + (j % (R_TJ / 2)) * 16 + lr;
+    else
+      row = wn * (TBN / RWN) + j * 16 + lr;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) b_off[h][j] = row * 128 + ((h * 4 + lane / 16) ^ ((row >> 1) & 7)) * 16;
+  }
+  const int ni = min(R_TI, (w.M - w.m0 + 15) / 16);
+
+  f32x4 acc[R_TI][R_TJ];
+#pragma unroll
+  for (int i = 0; i < R_TI; ++i)
+#pragma unroll
+    for (int j = 0; j < R_TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nb = K / 64;
+  issue_a(0);
+  issue_b(0);
+  auto k_loop = [&](auto live) {
+    constexpr int NI = decltype(live)::value;
+    auto step = [&](const unsigned char* as, const unsigned char* bs, int h) {
+      bf16x8 bfr[R_TJ], af[NI];
+#pragma unroll
+      for (int j = 0; j < R_TJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + b_off[h][j]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + a_off[i]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < R_TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    };
+    for (int jb = 0; jb < nb; ++jb) {
+      const unsigned char* bs = rlds + 2 * B::A_SLOT + (jb & 1) * B::B_SLOT;
+      const bool more = jb + 1 < nb;
+      // step 2jb: its activation step and weight block are the last loads issued.  After the
+      // barrier every wavefront is done with step 2jb-1, whose activation slot and (for the
+      // weights) block jb-1 are refilled next.
+      wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");
+      issue_a(2 * jb + 1);
+      if (more) issue_b(jb + 1);
+      step(rlds, bs, 0);
+      // step 2jb+1: complete once at most the next block's weight loads are pending
+      if (more)
+        wait_vmcnt<B::DMA_B>();
+      else
+        wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");
+      if (more) issue_a(2 * jb + 2);
+      step(rlds + B::A_SLOT, bs, 1);
+    }
+  };
+  static_assert(R_TI == 8, "one K-loop instance per live-slice count");
+  switch (ni) {
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    case 4: k_loop(std::integral_constant<int, 4>{}); break;
+    case 5: k_loop(std::integral_constant<int, 5>{}); break;
+    case 6: k_loop(std::integral_constant<int, 6>{}); break;
+    case 7: k_loop(std::integral_constant<int, 7>{}); break;
+    default: k_loop(std::integral_constant<int, 8>{}); break;
+  }
+
+  // epilogue: lane holds output channels 4*(lane/16) + v of tile row lane%16
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const int N = a.N;
+  const int c4 = 4 * (lane / 16);
+#pragma unroll
+  for (int i = 0; i < R_TI; ++i) {
+    const int m = w.m0 + i * 16 + lr;
+    if (m >= w.M) continue;
+    uint16_t* orow = out + (size_t)(w.r0 + m) * N;
+    if (MODE == 0) {
+#pragma unroll
+      for (int j = 0; j < R_TJ / 2; ++j) {
+        const int n = w.n0 + wn * (TBN / RWN / 2) + j * 16 + c4;  // N % 16 == 0: all 4 or none
+        if (n < N) {
+          const f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
+          *reinterpret_cast<uint2*>(orow + n) =
+              make_uint2(pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
+                         pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < R_TJ; ++j) {
+        const int n = w.n0 + wn * (TBN / RWN) + j * 16 + c4;
+        if (n < N) {
+          const f32x4 o = acc[i][j];
+          *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        }
+      }
+    }
+  }
+}
+
 // Raise a kernel's dynamic-LDS limit once per device (the attribute belongs to the current
 // device; the flags are indexed by device ordinal and safe to race on).
 constexpr int kMaxDevices = 64;
@@ -561,6 +739,15 @@ bool use_ring(const LayerDims& L) {
 
 template <int MODE, bool I8, int TBN>
 hipError_t run_ring(const GemmArgs& a, int grid, hipStream_t s) {
+  if constexpr (!I8) {
+    if (a.K % 64 == 0) {  // full-line weight blocks
+      static LdsFlags done64;
+      hipError_t e = set_lds(&k_gemm_ring64<MODE, TBN>, Ring64<TBN>::LDS, done64);
+      if (e != hipSuccess) return e;
+      return launch(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, k_gemm_ring64<MODE, TBN>, grid,
+                    R_THREADS, Ring64<TBN>::LDS, s, a);
+    }
+  }
   using B = RingB<I8, TBN>;
   static LdsFlags done;
   hipError_t e = set_lds(&k_gemm_ring<MODE, I8, TBN>, B::LDS, done);
@@ -603,7 +790,7 @@ struct TileRule {
 };
 constexpr TileRule kTileRules[] = {
     // DeepSeek-MoE-shaped layer: 64 routed experts of width 1408, top-6, 2 shared, d = 2048
-    {2048, 1408, 64, 6, 2, MOE_BF16, {{17, 64}, {128, 384}}, {{64, 128}, {384, 512}}},
+    {2048, 1408, 64, 6, 2, MOE_BF16, {{17, 64}, {1, 0}}, {{64, 128}, {1, 0}}},
     {2048, 1408, 64, 6, 2, MOE_I8, {{17, 32}, {1, 0}}, {{9, 128}, {1, 0}}},
 };
 
