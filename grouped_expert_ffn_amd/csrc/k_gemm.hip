@@ -790,7 +790,7 @@ struct TileRule {
 };
 constexpr TileRule kTileRules[] = {
     // DeepSeek-MoE-shaped layer: 64 routed experts of width 1408, top-6, 2 shared, d = 2048
-    {2048, 1408, 64, 6, 2, MOE_BF16, {{17, 64}, {1, 0}}, {{64, 128}, {1, 0}}},
+    {2048, 1408, 64, 6, 2, MOE_BF16, {{17, 48}, {1, 0}}, {{64, 128}, {1, 0}}},
     {2048, 1408, 64, 6, 2, MOE_I8, {{17, 32}, {1, 0}}, {{9, 128}, {1, 0}}},
 };
 
