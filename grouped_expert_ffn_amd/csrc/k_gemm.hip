@@ -27,11 +27,12 @@
 //    applied on the source side (each lane fetches a permuted 16-byte piece of its row).
 //    int8 weights are widened to bf16 (exact) as they are read from LDS, and the
 //    per-channel scales multiply the fp32 sums in the epilogue.
-//  * k_gemm_ring64 (bf16 weights, K a multiple of 64): the ring kernel's tiles, wavefronts
-//    and epilogue, with the weights staged 64 K deep (128 bytes, a whole cache line, of each
-//    row per block, so a DMA instruction covers 8 full lines instead of 16 half lines) in two
-//    slots, and the activations 32 K deep in two slots.  Used for bf16 weights whenever K
-//    allows; k_gemm_ring serves int8 weights and K % 64 == 32.
+//  * k_gemm_ring64 (bf16 or int8 weights, K a multiple of 64): the ring kernel's tiles,
+//    wavefronts and epilogue, with the weights staged 64 K deep in two slots (a bf16 row's
+//    block is 128 bytes, a whole cache line, so a DMA instruction covers 8 full lines instead
+//    of 16 half lines; an int8 row's block is 64 bytes, half lines instead of quarter lines)
+//    and the activations 32 K deep in two slots.  Used whenever K allows; k_gemm_ring serves
+//    K % 64 == 32.
 //  * k_gemm (any K that is a multiple of 16): 128x128 tiles, four wavefronts in a 2x2 layout
 //    each owning 64x64.  BK=64, LDS double buffer (rows padded by 16 bytes) with a register
 //    prefetch of the next K-step; int8 weights are widened to bf16 on the way into LDS.
@@ -542,29 +543,37 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ------------------------------------------------------------------------------------------
-// ring kernel with full-line weight blocks (bf16 weights, K % 64 == 0)
+// ring kernel with 64-deep weight blocks (K % 64 == 0)
 // ------------------------------------------------------------------------------------------
 // The same tile, wavefront layout, operand order and epilogue as k_gemm_ring, with the LDS
 // split into two 8 KiB activation slots (32 K per step) and two weight slots of 64 K per
-// block: 128 bytes of each weight row, one whole cache line, so one weight DMA instruction
-// covers 8 rows x 128 bytes instead of 16 rows x 64 bytes (half as many cache lines per
-// byte, which is what the weight path of the 32-deep ring pays for).  A weight block is
-// issued one block (two steps) ahead of its use, an activation step one step ahead.
-template <int TBN>
+// block.  A bf16 weight row gives a block 128 bytes, one whole cache line, so one weight DMA
+// instruction covers 8 rows x 128 bytes instead of 16 rows x 64 bytes; an int8 row gives 64
+// bytes (16 rows per instruction instead of 32 rows x 32 bytes).  Half as many cache lines
+// per weight byte, which is what the weight path of the 32-deep ring pays for.  A weight
+// block is issued one block (two steps) ahead of its use, an activation step one step ahead.
+template <bool W8, int TBN>
 struct Ring64 {
   static constexpr int TJ = TBN / RWN / 16;            // 16-column MFMA tiles per wavefront
   static constexpr int A_SLOT = R_A_BYTES;              // 128 rows x 64 bytes
-  static constexpr int B_SLOT = TBN * 128;              // TBN rows x 128 bytes
-  static constexpr int LDS = 2 * A_SLOT + 2 * B_SLOT;   // 80 KiB (256) / 48 KiB (128)
-  static constexpr int DMA_B = TBN / 8 / RWN;           // weight loads per block per wavefront
-  static constexpr int WAVES_PER_EU = 160 * 1024 / LDS >= 3 ? 3 : 2;
-  static_assert(DMA_B * 8 * RWN == TBN && TJ % 2 == 0, "tile split");
+  static constexpr int ROW = W8 ? 64 : 128;             // bytes of a weight row per block
+  static constexpr int B_SLOT = TBN * ROW;
+  static constexpr int LDS = 2 * A_SLOT + 2 * B_SLOT;   // bf16 80 / 48 KiB, int8 48 / 32 KiB
+  static constexpr int LPR = ROW / 16;                  // DMA lanes per weight row
+  static constexpr int RPI = 64 / LPR;                  // weight rows per DMA load
+  static constexpr int DMA_B = TBN / RPI / RWN;         // weight loads per block per wavefront
+  // 3 waves per SIMD only with 16 accumulator tiles per wavefront and room for 3 workgroups
+  static constexpr int WAVES_PER_EU = (TJ == 2 && 160 * 1024 / LDS >= 3) ? 3 : 2;
+  static_assert(DMA_B * RPI * RWN == TBN && TJ % 2 == 0, "tile split");
+  // 16-byte chunk swizzle of weight row r: keeps the 16 rows an operand read touches on
+  // distinct banks (8 chunks per bf16 row, 4 per int8 row)
+  static __device__ __forceinline__ int swz(int r) { return W8 ? (r >> 2) & 3 : (r >> 1) & 7; }
 };
 
-template <int MODE, int TBN>
+template <int MODE, bool W8, int TBN>
 __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
-    Ring64<TBN>::WAVES_PER_EU))) void k_gemm_ring64(const GemmArgs a) {
-  using B = Ring64<TBN>;
+    Ring64<W8, TBN>::WAVES_PER_EU))) void k_gemm_ring64(const GemmArgs a) {
+  using B = Ring64<W8, TBN>;
   constexpr int R_TJ = B::TJ;
   extern __shared__ __align__(16) unsigned char rlds[];
   Work w;
@@ -574,9 +583,8 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
 
   // Activation DMA as in k_gemm_ring: load q = wave*R_DMA_A + i fills rows 16q .. 16q+15,
   // lane l row 16q + l/4, 16-byte position l%4 with the row's chunk (l%4) ^ ((row >> 2) & 3).
-  // Weight DMA: load q = wave*DMA_B + i fills rows 8q .. 8q+7, lane l row 8q + l/8, 16-byte
-  // position l%8 with the row's chunk (l%8) ^ swzb(row), swzb(row) = (row >> 1) & 7, which
-  // keeps the 16 rows an MFMA operand read touches on distinct banks.
+  // Weight DMA: load q = wave*DMA_B + i fills rows RPI*q .. RPI*q + RPI-1, lane l row
+  // RPI*q + l/LPR, 16-byte position l%LPR with the row's chunk (l%LPR) ^ swz(row).
   const uint16_t* a_src[R_DMA_A];
   int ca[R_DMA_A];
 #pragma unroll
@@ -588,8 +596,8 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
   const unsigned char* b_src[B::DMA_B];
 #pragma unroll
   for (int i = 0; i < B::DMA_B; ++i) {
-    const int row = 8 * (wave * B::DMA_B + i) + lane / 8;
-    b_src[i] = b_row_t<MODE, TBN>(a, w, row, 2) + ((lane % 8) ^ ((row >> 1) & 7)) * 16;
+    const int row = B::RPI * (wave * B::DMA_B + i) + lane / B::LPR;
+    b_src[i] = b_row_t<MODE, TBN>(a, w, row, W8 ? 1 : 2) + ((lane % B::LPR) ^ B::swz(row)) * 16;
   }
   auto issue_a = [&](int kt) {  // step kt (32 K) into activation slot kt % 2
     unsigned char* st = rlds + (kt & 1) * B::A_SLOT;
@@ -602,7 +610,7 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     unsigned char* st = rlds + 2 * B::A_SLOT + (jb & 1) * B::B_SLOT;
 #pragma unroll
     for (int i = 0; i < B::DMA_B; ++i)
-      __builtin_amdgcn_global_load_lds((global_void*)(b_src[i] + jb * 128),
+      __builtin_amdgcn_global_load_lds((global_void*)(b_src[i] + jb * B::ROW),
                                        (lds_void*)(st + (wave * B::DMA_B + i) * 1024), 16, 0, 0);
   };
 
@@ -611,7 +619,8 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
   int a_off[R_TI];
 #pragma unroll
   for (int i = 0; i < R_TI; ++i) a_off[i] = (i * 16 + lr) * 64 + rd_chunk;
-  // weight operand of tile j in half h of a block: row r, logical chunk 4h + lane/16
+  // weight operand of tile j in half h of a block: row r, logical chunk c = 4h + lane/16 of
+  // the row's 16-byte (bf16) or 8-byte (int8) pieces
   int b_off[2][R_TJ];
 #pragma unroll
   for (int j = 0; j < R_TJ; ++j) {
@@ -621,7 +630,11 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     else
       row = wn * (TBN / RWN) + j * 16 + lr;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) b_off[h][j] = row * 128 + ((h * 4 + lane / 16) ^ ((row >> 1) & 7)) * 16;
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * 4 + lane / 16;
+      b_off[h][j] = W8 ? row * B::ROW + ((c >> 1) ^ B::swz(row)) * 16 + (c & 1) * 8
+                       : row * B::ROW + (c ^ B::swz(row)) * 16;
+    }
   }
   const int ni = min(R_TI, (w.M - w.m0 + 15) / 16);
 
@@ -639,7 +652,9 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     auto step = [&](const unsigned char* as, const unsigned char* bs, int h) {
       bf16x8 bfr[R_TJ], af[NI];
 #pragma unroll
-      for (int j = 0; j < R_TJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + b_off[h][j]);
+      for (int j = 0; j < R_TJ; ++j)
+        bfr[j] = W8 ? i8x8_to_bf16x8(*reinterpret_cast<const uint2*>(bs + b_off[h][j]))
+                    : *reinterpret_cast<const bf16x8*>(bs + b_off[h][j]);
 #pragma unroll
       for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + a_off[i]);
 #pragma unroll
@@ -695,7 +710,13 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
       for (int j = 0; j < R_TJ / 2; ++j) {
         const int n = w.n0 + wn * (TBN / RWN / 2) + j * 16 + c4;  // N % 16 == 0: all 4 or none
         if (n < N) {
-          const f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
+          f32x4 g = acc[i][j], u = acc[i][j + R_TJ / 2];
+          if (W8) {  // per-channel scales on the fp32 sums
+            const float4 sg = *reinterpret_cast<const float4*>(a.s0 + (size_t)w.g * N + n);
+            const float4 su = *reinterpret_cast<const float4*>(a.s1 + (size_t)w.g * N + n);
+            g = g * f32x4{sg.x, sg.y, sg.z, sg.w};
+            u = u * f32x4{su.x, su.y, su.z, su.w};
+          }
           *reinterpret_cast<uint2*>(orow + n) =
               make_uint2(pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
                          pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]));
@@ -706,7 +727,11 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
       for (int j = 0; j < R_TJ; ++j) {
         const int n = w.n0 + wn * (TBN / RWN) + j * 16 + c4;
         if (n < N) {
-          const f32x4 o = acc[i][j];
+          f32x4 o = acc[i][j];
+          if (W8) {
+            const float4 sd = *reinterpret_cast<const float4*>(a.s0 + (size_t)w.g * N + n);
+            o = o * f32x4{sd.x, sd.y, sd.z, sd.w};
+          }
           *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
       }
@@ -739,14 +764,12 @@ bool use_ring(const LayerDims& L) {
 
 template <int MODE, bool I8, int TBN>
 hipError_t run_ring(const GemmArgs& a, int grid, hipStream_t s) {
-  if constexpr (!I8) {
-    if (a.K % 64 == 0) {  // full-line weight blocks
-      static LdsFlags done64;
-      hipError_t e = set_lds(&k_gemm_ring64<MODE, TBN>, Ring64<TBN>::LDS, done64);
-      if (e != hipSuccess) return e;
-      return launch(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, k_gemm_ring64<MODE, TBN>, grid,
-                    R_THREADS, Ring64<TBN>::LDS, s, a);
-    }
+  if (a.K % 64 == 0) {  // 64-deep weight blocks
+    static LdsFlags done64;
+    hipError_t e = set_lds(&k_gemm_ring64<MODE, I8, TBN>, Ring64<I8, TBN>::LDS, done64);
+    if (e != hipSuccess) return e;
+    return launch(MODE == 0 ? MOE_KERNEL_GATE_UP : MOE_KERNEL_DOWN, k_gemm_ring64<MODE, I8, TBN>, grid,
+                  R_THREADS, Ring64<I8, TBN>::LDS, s, a);
   }
   using B = RingB<I8, TBN>;
   static LdsFlags done;
@@ -791,7 +814,7 @@ struct TileRule {
 constexpr TileRule kTileRules[] = {
     // DeepSeek-MoE-shaped layer: 64 routed experts of width 1408, top-6, 2 shared, d = 2048
     {2048, 1408, 64, 6, 2, MOE_BF16, {{17, 48}, {1, 0}}, {{64, 128}, {1, 0}}},
-    {2048, 1408, 64, 6, 2, MOE_I8, {{17, 32}, {1, 0}}, {{9, 128}, {1, 0}}},
+    {2048, 1408, 64, 6, 2, MOE_I8, {{25, 32}, {1, 0}}, {{9, 512}, {1, 0}}},
 };
 
 // N-tile width of the ring kernel for one matrix (mode 0 gate/up, 1 down) of a layer at T tokens.
