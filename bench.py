@@ -57,7 +57,10 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=16,
+                   help="untimed steps before the timed ones (the default touches each of the 8 "
+                        "weight copies twice: a copy's first pass pays page-table walks, and the "
+                        "clocks settle)")
     p.add_argument("--workload", default="olmoe_bf16")
     p.add_argument("--tokens", type=int, default=8)
     p.add_argument("--copies", type=int, default=8, help="weight replicas rotated over (cache defeat)")
@@ -543,7 +546,7 @@ def measure_capacity(wl, T, cf, steps, copies):
     pt = Point(wl, T, copies, cf=cf)
     ids = pt.sanity_gate()
     cap, dropped = drop_stats(ids, wl.E, cf)
-    ms, _ = time_steps(pt.step, steps, 3)
+    ms, _ = time_steps(pt.step, steps, 2 * copies)
     pt.free()
     counts = np.bincount(ids.ravel(), minlength=wl.E)
     return {"workload": wl.name, "tokens": T, "capacity_factor": cf, "capacity_rows": cap,
@@ -653,7 +656,7 @@ def main():
         name, t = item.split(":")
         if name == wl.name and int(t) == args.tokens:
             continue
-        r, rf, *_ = measure(S.WORKLOADS[name], int(t), args.sweep_steps, 3, args.copies)
+        r, rf, *_ = measure(S.WORKLOADS[name], int(t), args.sweep_steps, 2 * args.copies, args.copies)
         r["roofline_frac"] = rf["frac"]
         r["roofline_bound"] = rf["bound"]
         sweep.append(r)
