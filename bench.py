@@ -146,6 +146,28 @@ def time_steps(step, steps, warmup):
     return ev0.elapsed_time(ev1) / steps, wall
 
 
+def warm_up(step, copies, min_s=0.05):
+    """Untimed steps for the sweep and capacity points: two rotations over the weight copies,
+    then more until at least `min_s` seconds of GPU work have run (the first passes over a
+    copy pay page-table walks, and the clocks take tens of ms to settle).  Returns the count."""
+    import torch
+    n = 2 * copies
+    for i in range(n):
+        step(i)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(copies):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    n += copies
+    per_step = max(ev0.elapsed_time(ev1) / copies * 1e-3, 1e-6)
+    extra = max(0, int(min_s / per_step) - n)
+    for i in range(extra):
+        step(i)
+    return n + extra
+
+
 def step_percentiles(step, n):
     """p10 / median / p90 of single steps, each bracketed by its own event pair."""
     import numpy as np
@@ -394,6 +416,7 @@ def _fracs(work, ms):
 
 
 def measure(wl, T, steps, warmup, copies, extras=False):
+    """warmup: untimed steps before the timed ones, or None for warm_up()'s count."""
     import numpy as np
 
     from grouped_expert_ffn_amd import abi
@@ -401,6 +424,9 @@ def measure(wl, T, steps, warmup, copies, extras=False):
     ids = pt.sanity_gate()
     n_touched = int(np.count_nonzero(np.bincount(ids.ravel(), minlength=wl.E)))
     work = layer_work(wl, T, n_touched)
+    if warmup is None:
+        warm_up(pt.step, copies)
+        warmup = 0
     ms, wall = time_steps(pt.step, steps, warmup)
     launches = max(10, min(steps, 50))
     gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, pt.step, launches)
@@ -505,7 +531,8 @@ def measure_stack(wl, steps):
     st = Stack(wl, wl.tokens[0])
     st.sanity_gate()
     T, n = st.T, wl.n_layers
-    ms, _ = time_steps(st.step, steps, 2)
+    warm_up(st.step, 1)
+    ms, _ = time_steps(st.step, steps, 0)
     gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, st.layer, 2 * n)
     dn_ms, _ = time_kernel(abi.MOE_KERNEL_DOWN, st.layer, 2 * n)
     work = layer_work(wl, T, wl.E)  # every expert is touched at T=2048
@@ -546,7 +573,8 @@ def measure_capacity(wl, T, cf, steps, copies):
     pt = Point(wl, T, copies, cf=cf)
     ids = pt.sanity_gate()
     cap, dropped = drop_stats(ids, wl.E, cf)
-    ms, _ = time_steps(pt.step, steps, 2 * copies)
+    warm_up(pt.step, copies)
+    ms, _ = time_steps(pt.step, steps, 0)
     pt.free()
     counts = np.bincount(ids.ravel(), minlength=wl.E)
     return {"workload": wl.name, "tokens": T, "capacity_factor": cf, "capacity_rows": cap,
@@ -656,7 +684,7 @@ def main():
         name, t = item.split(":")
         if name == wl.name and int(t) == args.tokens:
             continue
-        r, rf, *_ = measure(S.WORKLOADS[name], int(t), args.sweep_steps, 2 * args.copies, args.copies)
+        r, rf, *_ = measure(S.WORKLOADS[name], int(t), args.sweep_steps, None, args.copies)
         r["roofline_frac"] = rf["frac"]
         r["roofline_bound"] = rf["bound"]
         sweep.append(r)
