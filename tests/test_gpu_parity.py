@@ -192,8 +192,11 @@ SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     (S.OLMOE_BF16, 64), (S.OLMOE_I8, 64), (S.OLMOE_I8_ZIPF, 64), (S.DEEPSEEK_BF16, 16),
     (S.DEEPSEEK_BF16, 128), (S.DEEPSEEK_BF16, 512), (S.DEEPSEEK_BF16, 2048), (S.DEEPSEEK_I8, 16),
     (S.DEEPSEEK_I8, 512),
-    # the tuned tile widths: gate/up 128 + down 256, gate/up 256 + down 128 (bf16 and int8)
-    (S.DEEPSEEK_BF16, 40), (S.DEEPSEEK_BF16, 450), (S.DEEPSEEK_I8, 24), (S.DEEPSEEK_I8, 100),
+    # the tuned tile widths (bf16: gate/up 128 at T = 17-48, down 128 at T = 64-128; int8:
+    # gate/up 128 at T = 25-32, down 128 at T = 9-512): bf16 gate/up 128 + down 256, gate/up
+    # 256 + down 128, both 256; int8 gate/up 256 + down 128, both 128
+    (S.DEEPSEEK_BF16, 40), (S.DEEPSEEK_BF16, 100), (S.DEEPSEEK_BF16, 450), (S.DEEPSEEK_I8, 24),
+    (S.DEEPSEEK_I8, 30), (S.DEEPSEEK_I8, 100),
     # the GEMV at its largest sizes (routed experts only: groups of several 4-row chunks)
     (S.OLMOE_BF16, 32), (S.OLMOE_I8, 16),
 ]
