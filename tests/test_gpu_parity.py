@@ -170,6 +170,10 @@ SMALL_RING = S.Workload("small_ring", 93, d=288, E=8, k=2, I=352, S=1, renormali
 # both GEMMs (I=448 is 3.5 gate/up tiles of 128 channels, d=320 is 1.25 down tiles of 256)
 SMALL_RING64 = S.Workload("small_ring64", 99, d=320, E=8, k=2, I=448, S=1, renormalize=True,
                           tokens=(300,))
+# int8 weights on both ring kernels: the 32-deep ring serves K % 64 == 32 (SMALL_RING's
+# d=288 and I=352), the 64-deep blocks K % 64 == 0
+SMALL_RING_I8 = dataclasses.replace(SMALL_RING, name="small_ring_i8", cid=88, wdt="i8")
+SMALL_RING64_I8 = dataclasses.replace(SMALL_RING64, name="small_ring64_i8", cid=89, wdt="i8")
 
 # the limits of the descriptor: 256 experts, top-16, 8 shared experts, and the smallest
 # dimensions (d = I = 16; neither a multiple of the 32-wide K step of the ring GEMM)
@@ -181,7 +185,7 @@ FULL_CASES = [  # every row checked
     (EDGE_MAX, 4), (EDGE_MAX, 40), (EDGE_MIN, 5), (EDGE_MIN, 40), (S.TINY_F32, 200),
     (S.TINY_F32, 16), (SMALL_RAGGED, 100), (SMALL_RAGGED, 7), (SMALL_RAGGED_I8, 100),
     (SMALL_RAGGED_I8, 5), (SMALL_ZIPF, 300), (SMALL_RING, 300), (SMALL_RING, 40),
-    (SMALL_RING64, 300), (SMALL_RING64, 40),
+    (SMALL_RING64, 300), (SMALL_RING64, 40), (SMALL_RING_I8, 300), (SMALL_RING64_I8, 300),
     (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8),
     # speculative-decode verify batches (draft length + 1 tokens): T = 3 on the GEMV,
     # T = 9 the first size on the matrix-core GEMM
