@@ -261,7 +261,9 @@ def test_steps_sampled(wl, T):
     _steps_and_check(wl, T, sampled=True)
 
 
+# moe_forward against the five step-by-step calls, bit for bit, at decode and prefill sizes
 @pytest.mark.parametrize("wl,T", [(S.TINY_F32, 16), (SMALL_RAGGED, 100), (S.OLMOE_BF16, 8),
+                                  (S.OLMOE_BF16, 1), (S.DEEPSEEK_BF16, 4), (S.OLMOE_I8, 8),
                                   (S.DEEPSEEK_BF16, 512), (S.OLMOE_I8, 64)], ids=case_id)
 def test_forward_matches_steps_and_is_deterministic(wl, T):
     from grouped_expert_ffn_amd import to_device
@@ -281,11 +283,11 @@ def test_forward_matches_steps_and_is_deterministic(wl, T):
     assert t.equal(y1, steps["y"])
 
 
-def test_forward_residual_and_power_of_two_scaling():
+@pytest.mark.parametrize("T", [4, 16])  # the decode GEMV and the prefill GEMM
+def test_forward_residual_and_power_of_two_scaling(T):
     from grouped_expert_ffn_amd import DeviceLayer, to_device
     t = T_()
     wl = S.DEEPSEEK_BF16
-    T = 16
     gl = C.GpuLayer(wl)
     xd = to_device(S.make_tokens(wl, T))
     y = gl.dev.forward(xd)
