@@ -831,7 +831,7 @@ int ring_tile_n(const LayerDims& L, int T, int mode) {
 
 int gemm_tile_m(const LayerDims& L) { return use_ring(L) ? RBM : BM; }
 
-hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
+hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s, int which) {
   const bool ring = use_ring(L);
   const int tm = ring ? RBM : BM;
   const int max_tiles = (int)plan_max_tiles(T, L.k, L.E, L.S);
@@ -857,8 +857,11 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.K = L.d;
   a.N = L.I;
   int tbn = ring ? ring_tile_n(L, T, 0) : 0;
-  err = i8 ? run_gemm<0, true>(a, grid_tiles, tbn, s) : run_gemm<0, false>(a, grid_tiles, tbn, s);
-  if (err != hipSuccess) return err;
+  if (which & kFfnGateUp) {
+    err = i8 ? run_gemm<0, true>(a, grid_tiles, tbn, s) : run_gemm<0, false>(a, grid_tiles, tbn, s);
+    if (err != hipSuccess) return err;
+  }
+  if (!(which & kFfnDown)) return hipSuccess;
 
   a.in = f.h;
   a.w0 = f.w_down;

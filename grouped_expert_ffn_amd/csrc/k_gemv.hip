@@ -334,7 +334,7 @@ hipError_t dispatch_gemv(const GemvArgs& a, int T, int slots, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
+hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s, int which) {
   const int slots = (T * L.k < L.E ? T * L.k : L.E) + L.S;
   GemvArgs a{};
   a.offsets = f.offsets;
@@ -353,13 +353,16 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.h;
   a.K = L.d;
   a.N = L.I;
-  if (L.act == MOE_F32)
-    err = dispatch_gemv<0, float, float>(a, T, slots, s);
-  else if (L.wdt == MOE_I8)
-    err = dispatch_gemv<0, uint16_t, int8_t>(a, T, slots, s);
-  else
-    err = dispatch_gemv<0, uint16_t, uint16_t>(a, T, slots, s);
-  if (err != hipSuccess) return err;
+  if (which & kFfnGateUp) {
+    if (L.act == MOE_F32)
+      err = dispatch_gemv<0, float, float>(a, T, slots, s);
+    else if (L.wdt == MOE_I8)
+      err = dispatch_gemv<0, uint16_t, int8_t>(a, T, slots, s);
+    else
+      err = dispatch_gemv<0, uint16_t, uint16_t>(a, T, slots, s);
+    if (err != hipSuccess) return err;
+  }
+  if (!(which & kFfnDown)) return hipSuccess;
 
   // down
   a.in = f.h;

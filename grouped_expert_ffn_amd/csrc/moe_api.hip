@@ -170,8 +170,20 @@ int ffn_tile_m(const LayerDims& L, int T) {
   return T > gemv_max ? gemm_tile_m(L) : 0;
 }
 
+// Just past the GEMV's range with shared experts, the down projection (K = I, the shared
+// experts' T rows in a few passes of 4) still streams faster on the GEMV while gate/up is
+// faster on the GEMM: DeepSeek shapes, bf16, down 27.9 / 29.4 us on the GEMV against 33.9 /
+// 35.7 us on the GEMM at T = 9 / 12, gate/up 51.6 / 55.7 against 47.0 / 51.6 us; at T = 16 and
+// with int8 weights the two tie.  The launch plan serves both (the GEMV ignores its tiles).
+constexpr int kGemvDownMaxTokensShared = 12;
+
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s) {
-  return ffn_tile_m(L, T) ? launch_gemm_ffn(L, T, a, s) : launch_gemv_ffn(L, T, a, s);
+  if (!ffn_tile_m(L, T)) return launch_gemv_ffn(L, T, a, s);
+  if (L.S > 0 && L.wdt == MOE_BF16 && T <= kGemvDownMaxTokensShared) {
+    hipError_t e = launch_gemm_ffn(L, T, a, s, kFfnGateUp);
+    return e != hipSuccess ? e : launch_gemv_ffn(L, T, a, s, kFfnDown);
+  }
+  return launch_gemm_ffn(L, T, a, s);
 }
 
 }  // namespace moe

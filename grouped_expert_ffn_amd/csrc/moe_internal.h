@@ -202,8 +202,12 @@ struct FfnArgs {
 // M-tile height the grouped FFN will use for T tokens (0: GEMV path, no tile list needed).
 int ffn_tile_m(const LayerDims& L, int T);
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
-hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
-hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+// which: kFfnGateUp | kFfnDown, the matrices to launch
+constexpr int kFfnGateUp = 1, kFfnDown = 2;
+hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s,
+                           int which = kFfnGateUp | kFfnDown);
+hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s,
+                           int which = kFfnGateUp | kFfnDown);
 int gemm_tile_m(const LayerDims& L);
 
 hipError_t launch_combine(const LayerDims& L, int T, const void* rows, const int32_t* inv_perm,

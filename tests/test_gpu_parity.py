@@ -203,6 +203,8 @@ SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     (S.DEEPSEEK_I8, 30), (S.DEEPSEEK_I8, 100),
     # the GEMV at its largest sizes (routed experts only: groups of several 4-row chunks)
     (S.OLMOE_BF16, 32), (S.OLMOE_I8, 16),
+    # gate/up on the MFMA GEMM, down on the GEMV (bf16 with shared experts, T = 9-12)
+    (S.DEEPSEEK_BF16, 9), (S.DEEPSEEK_BF16, 12),
 ]
 
 
