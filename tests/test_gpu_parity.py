@@ -205,6 +205,8 @@ SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     (S.OLMOE_BF16, 32), (S.OLMOE_I8, 16),
     # gate/up on the MFMA GEMM, down on the GEMV (bf16 with shared experts, T = 9-12)
     (S.DEEPSEEK_BF16, 9), (S.DEEPSEEK_BF16, 12),
+    # the sweep's largest points on the other shapes (64-deep weight blocks, bf16 and int8)
+    (S.OLMOE_BF16, 2048), (S.OLMOE_I8, 2048), (S.DEEPSEEK_I8, 2048),
 ]
 
 
