@@ -364,19 +364,6 @@ struct RingB {
   static_assert((NST - 2) * LPS < 64 && NST >= 3 && NST <= 6, "vmcnt range");
 };
 
-// 8 int8 weights -> 8 bf16 (exact for |q| <= 127)
-__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(const uint2& q) {
-  uint32_t o[4];
-  const uint32_t w[2] = {q.x, q.y};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int32_t v = (int32_t)w[i];
-    o[2 * i] = pack_bf16x2((float)((v << 24) >> 24), (float)((v << 16) >> 24));
-    o[2 * i + 1] = pack_bf16x2((float)((v << 8) >> 24), (float)(v >> 24));
-  }
-  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
-}
-
 template <int MODE, bool W8, int TBN>
 __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     RingB<W8, TBN>::WAVES_PER_EU))) void k_gemm_ring(const GemmArgs a) {
@@ -831,7 +818,7 @@ int ring_tile_n(const LayerDims& L, int T, int mode) {
 
 int gemm_tile_m(const LayerDims& L) { return use_ring(L) ? RBM : BM; }
 
-hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s, int which) {
+hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
   const bool ring = use_ring(L);
   const int tm = ring ? RBM : BM;
   const int max_tiles = (int)plan_max_tiles(T, L.k, L.E, L.S);
@@ -857,11 +844,8 @@ hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.K = L.d;
   a.N = L.I;
   int tbn = ring ? ring_tile_n(L, T, 0) : 0;
-  if (which & kFfnGateUp) {
-    err = i8 ? run_gemm<0, true>(a, grid_tiles, tbn, s) : run_gemm<0, false>(a, grid_tiles, tbn, s);
-    if (err != hipSuccess) return err;
-  }
-  if (!(which & kFfnDown)) return hipSuccess;
+  err = i8 ? run_gemm<0, true>(a, grid_tiles, tbn, s) : run_gemm<0, false>(a, grid_tiles, tbn, s);
+  if (err != hipSuccess) return err;
 
   a.in = f.h;
   a.w0 = f.w_down;

@@ -153,37 +153,58 @@ LaunchTimer::~LaunchTimer() {
   if (stop_) (void)hipEventRecord(stop_, s_);
 }
 
-constexpr int kGemvMaxTokens = 8;           // with shared experts
-constexpr int kGemvMaxTokensRouted = 32;    // routed experts only, bf16 weights
-constexpr int kGemvMaxTokensRoutedI8 = 16;  // routed experts only, int8 weights
+// Which kernel family serves a layer's two FFN launches at T tokens.  Three regimes, by the
+// rows a group holds (a routed expert T*k/E on average, a shared expert all T):
+//  * the VALU GEMV while groups hold a few rows: its dot products cost less than the matrix
+//    cores' 16-token tiles (OLMoE shapes: gate/up at T=8 66.5 against 69.3 us on the
+//    matrix-core GEMV, int8 36 against 42 us);
+//  * the matrix-core GEMV (same weight streaming, MFMA math, rows in chunks of 16) while the
+//    groups stay within a chunk or two: OLMoE layer -4% at T=32, -13% at T=48, -11% at T=64
+//    against the GEMM, even at T=128 (+2%); int8 -7% at T=24, -2% at 48, +1% at 64.  With
+//    shared experts (DeepSeek shapes) from T=8 (-4% against the VALU GEMV) to T=16 (-7%
+//    against the GEMM; -9 to -10% at T=9 and 12; +3% at T=32, where a shared expert's 32
+//    rows take two chunks); int8 -7% at T=8 and 16;
+//  * the LDS-ring GEMM beyond.
+// The matrix-core GEMV needs bf16 activations and d, I multiples of 64; other layers keep
+// the VALU GEMV up to 8 tokens with shared experts, 32 (bf16 weights) or 16 (int8) without.
+enum class FfnPath { kGemv, kGemvMfma, kGemm };
 
-int ffn_tile_m(const LayerDims& L, int T) {
-  if (L.act == MOE_F32) return 0;
-  // The GEMV streams each group's weights once and does its rows in passes of a few rows.
-  // A shared expert holds all T rows, so past 8 tokens it needs several passes and the
-  // matrix-core GEMM is as fast or faster (DeepSeek shapes: equal layer time at T = 9 and
-  // 12, 15% faster at 16).  With routed experts only, groups stay small: on the OLMoE shapes
-  // the GEMV is faster up to 32 tokens with bf16 weights (-8% at T = 24, -3% at 32, +9% at
-  // 48) and up to 16 with int8 weights (the GEMM is 3% faster at 32).
-  const int gemv_max = L.S > 0 ? kGemvMaxTokens
-                               : (L.wdt == MOE_I8 ? kGemvMaxTokensRoutedI8 : kGemvMaxTokensRouted);
-  return T > gemv_max ? gemm_tile_m(L) : 0;
+constexpr int kGemvMaxTokensShared = 7;     // VALU GEMV with shared experts
+constexpr int kGemvRowsRouted = 3;          // VALU GEMV without: mean rows per routed group,
+constexpr int kGemvRowsRoutedI8 = 2;        //   bf16 / int8 weights
+constexpr int kMfmaMaxTokensShared = 16;    // matrix-core GEMV with shared experts
+constexpr int kMfmaRowsRouted = 8;          // matrix-core GEMV without: mean rows per group
+constexpr int kMfmaRowsRoutedI8 = 6;
+constexpr int kGemvMaxTokensNoMfma[2] = {32, 16};  // layers the matrix-core GEMV cannot take:
+constexpr int kGemvMaxTokensNoMfmaShared = 8;      //   VALU GEMV limits (bf16, int8 weights)
+
+FfnPath ffn_path(const LayerDims& L, int T) {
+  if (L.act == MOE_F32) return FfnPath::kGemv;
+  const bool i8 = L.wdt == MOE_I8;
+  const long tk = (long)T * L.k, E = L.E;
+  if (L.d % 64 != 0 || L.I % 64 != 0) {
+    const int gemv_max = L.S > 0 ? kGemvMaxTokensNoMfmaShared : kGemvMaxTokensNoMfma[i8];
+    return T > gemv_max ? FfnPath::kGemm : FfnPath::kGemv;
+  }
+  if (L.S > 0) {
+    if (T <= kGemvMaxTokensShared) return FfnPath::kGemv;
+    return T <= kMfmaMaxTokensShared ? FfnPath::kGemvMfma : FfnPath::kGemm;
+  }
+  if (tk <= (i8 ? kGemvRowsRoutedI8 : kGemvRowsRouted) * E) return FfnPath::kGemv;
+  return tk <= (i8 ? kMfmaRowsRoutedI8 : kMfmaRowsRouted) * E ? FfnPath::kGemvMfma : FfnPath::kGemm;
 }
 
-// Just past the GEMV's range with shared experts, the down projection (K = I, the shared
-// experts' T rows in a few passes of 4) still streams faster on the GEMV while gate/up is
-// faster on the GEMM: DeepSeek shapes, bf16, down 27.9 / 29.4 us on the GEMV against 33.9 /
-// 35.7 us on the GEMM at T = 9 / 12, gate/up 51.6 / 55.7 against 47.0 / 51.6 us; at T = 16 and
-// with int8 weights the two tie.  The launch plan serves both (the GEMV ignores its tiles).
-constexpr int kGemvDownMaxTokensShared = 12;
+// The launch plan carries M-tiles only for the GEMM; both GEMVs read its group list alone.
+int ffn_tile_m(const LayerDims& L, int T) {
+  return ffn_path(L, T) == FfnPath::kGemm ? gemm_tile_m(L) : 0;
+}
 
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s) {
-  if (!ffn_tile_m(L, T)) return launch_gemv_ffn(L, T, a, s);
-  if (L.S > 0 && L.wdt == MOE_BF16 && T <= kGemvDownMaxTokensShared) {
-    hipError_t e = launch_gemm_ffn(L, T, a, s, kFfnGateUp);
-    return e != hipSuccess ? e : launch_gemv_ffn(L, T, a, s, kFfnDown);
+  switch (ffn_path(L, T)) {
+    case FfnPath::kGemv: return launch_gemv_ffn(L, T, a, s);
+    case FfnPath::kGemvMfma: return launch_gemv_mfma_ffn(L, T, a, s);
+    default: return launch_gemm_ffn(L, T, a, s);
   }
-  return launch_gemm_ffn(L, T, a, s);
 }
 
 }  // namespace moe

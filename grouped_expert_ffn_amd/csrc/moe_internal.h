@@ -45,6 +45,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
+// 8 int8 weights -> 8 bf16 (exact for |q| <= 127)
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(const uint2& q) {
+  uint32_t o[4];
+  const uint32_t w[2] = {q.x, q.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int32_t v = (int32_t)w[i];
+    o[2 * i] = pack_bf16x2((float)((v << 24) >> 24), (float)((v << 16) >> 24));
+    o[2 * i + 1] = pack_bf16x2((float)((v << 8) >> 24), (float)(v >> 24));
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Activation element access for the two activation types.
@@ -199,15 +212,14 @@ struct FfnArgs {
   void* h;
   void* rows;
 };
-// M-tile height the grouped FFN will use for T tokens (0: GEMV path, no tile list needed).
+// M-tile height the grouped FFN will use for T tokens (0: a GEMV path, no tile list needed).
 int ffn_tile_m(const LayerDims& L, int T);
 hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
-// which: kFfnGateUp | kFfnDown, the matrices to launch
-constexpr int kFfnGateUp = 1, kFfnDown = 2;
-hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s,
-                           int which = kFfnGateUp | kFfnDown);
-hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s,
-                           int which = kFfnGateUp | kFfnDown);
+// the FFN's two launches (gate/up + SwiGLU, then down) on one kernel family: the VALU GEMV,
+// the matrix-core GEMV (bf16 activations, d and I multiples of 64), the MFMA GEMM
+hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+hipError_t launch_gemv_mfma_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
 int gemm_tile_m(const LayerDims& L);
 
 hipError_t launch_combine(const LayerDims& L, int T, const void* rows, const int32_t* inv_perm,

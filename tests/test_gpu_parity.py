@@ -175,6 +175,13 @@ SMALL_RING64 = S.Workload("small_ring64", 99, d=320, E=8, k=2, I=448, S=1, renor
 SMALL_RING_I8 = dataclasses.replace(SMALL_RING, name="small_ring_i8", cid=88, wdt="i8")
 SMALL_RING64_I8 = dataclasses.replace(SMALL_RING64, name="small_ring64_i8", cid=89, wdt="i8")
 
+# the matrix-core GEMV (bf16 activations, d and I multiples of 64): routed experts only under
+# Zipf routing, so the busiest groups span two 16-token chunks (T=32: 64 rows over 8 experts);
+# T=12 is the last size on the VALU GEMV (mean 3 rows per group), T=13 the first on this one
+SMALL_MFV = S.Workload("small_mfv", 86, d=320, E=8, k=2, I=448, S=0, renormalize=True,
+                       routing="zipf", zipf_alpha=2.0, router_std=0.05, tokens=(32,))
+SMALL_MFV_I8 = dataclasses.replace(SMALL_MFV, name="small_mfv_i8", cid=85, wdt="i8")
+
 # the limits of the descriptor: 256 experts, top-16, 8 shared experts, and the smallest
 # dimensions (d = I = 16; neither a multiple of the 32-wide K step of the ring GEMM)
 EDGE_MAX = S.Workload("edge_max", 95, d=48, E=256, k=16, I=48, S=8, renormalize=True,
@@ -191,6 +198,10 @@ FULL_CASES = [  # every row checked
     # T = 9 the first size on the matrix-core GEMM
     (S.OLMOE_BF16, 3), (S.OLMOE_BF16, 9),
     (S.OLMOE_I8, 1), (S.OLMOE_I8, 8), (S.DEEPSEEK_BF16, 1), (S.OLMOE_I8_ZIPF, 8),
+    # the matrix-core GEMV: ragged Zipf groups (bf16 and int8), its lower edge, and with a
+    # shared expert (T = 8-16; the shared group is one full chunk at T=16)
+    (SMALL_MFV, 32), (SMALL_MFV, 13), (SMALL_MFV, 12), (SMALL_MFV_I8, 24), (SMALL_RING64, 12),
+    (SMALL_RING64_I8, 16),
 ]
 SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     (S.OLMOE_BF16, 64), (S.OLMOE_I8, 64), (S.OLMOE_I8_ZIPF, 64), (S.DEEPSEEK_BF16, 16),
@@ -201,10 +212,12 @@ SAMPLED_CASES = [  # rows sampled (tile edges, segment ends, random)
     # 256 + down 128, both 256; int8 gate/up 256 + down 128, both 128
     (S.DEEPSEEK_BF16, 40), (S.DEEPSEEK_BF16, 100), (S.DEEPSEEK_BF16, 450), (S.DEEPSEEK_I8, 24),
     (S.DEEPSEEK_I8, 30), (S.DEEPSEEK_I8, 100),
-    # the GEMV at its largest sizes (routed experts only: groups of several 4-row chunks)
-    (S.OLMOE_BF16, 32), (S.OLMOE_I8, 16),
-    # gate/up on the MFMA GEMM, down on the GEMV (bf16 with shared experts, T = 9-12)
-    (S.DEEPSEEK_BF16, 9), (S.DEEPSEEK_BF16, 12),
+    # the VALU GEMV at its largest sizes (routed experts only: groups of several 4-row chunks)
+    (S.OLMOE_BF16, 24), (S.OLMOE_I8, 16),
+    # the matrix-core GEMV on the production shapes (OLMoE bf16 T = 25-64, int8 17-48;
+    # DeepSeek T = 8-16; OLMOE_BF16 64 and DEEPSEEK 16 above)
+    (S.OLMOE_BF16, 32), (S.OLMOE_I8, 48), (S.OLMOE_I8_ZIPF, 24), (S.DEEPSEEK_BF16, 8),
+    (S.DEEPSEEK_BF16, 9), (S.DEEPSEEK_BF16, 12), (S.DEEPSEEK_I8, 8),
     # the sweep's largest points on the other shapes (64-deep weight blocks, bf16 and int8)
     (S.OLMOE_BF16, 2048), (S.OLMOE_I8, 2048), (S.DEEPSEEK_I8, 2048),
 ]
@@ -447,7 +460,7 @@ def test_permute_with_capacity_is_bit_exact(T, E, k, S_, cf):
 
 CAP_CASES = [(SMALL_ZIPF, 300, 1.0), (SMALL_RING, 300, 1.0), (SMALL_RING, 40, 0.5),
              (S.OLMOE_BF16, 8, 1.0), (S.OLMOE_I8_ZIPF, 8, 1.0), (S.DEEPSEEK_BF16, 2048, 1.0),
-             (S.DEEPSEEK_BF16, 16, 2.0)]
+             (S.DEEPSEEK_BF16, 16, 2.0), (SMALL_MFV, 32, 1.0)]
 
 
 @pytest.mark.parametrize("wl,T,cf", CAP_CASES, ids=case_id)
