@@ -194,8 +194,7 @@ FULL_CASES = [  # every row checked
     (SMALL_RAGGED_I8, 5), (SMALL_ZIPF, 300), (SMALL_RING, 300), (SMALL_RING, 40),
     (SMALL_RING64, 300), (SMALL_RING64, 40), (SMALL_RING_I8, 300), (SMALL_RING64_I8, 300),
     (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8),
-    # speculative-decode verify batches (draft length + 1 tokens): T = 3 on the GEMV,
-    # T = 9 the first size on the matrix-core GEMM
+    # speculative-decode verify batches (draft length + 1 tokens), both on the VALU GEMV
     (S.OLMOE_BF16, 3), (S.OLMOE_BF16, 9),
     (S.OLMOE_I8, 1), (S.OLMOE_I8, 8), (S.DEEPSEEK_BF16, 1), (S.OLMOE_I8_ZIPF, 8),
     # the matrix-core GEMV: ragged Zipf groups (bf16 and int8), its lower edge, and with a
