@@ -160,7 +160,7 @@ LaunchTimer::~LaunchTimer() {
 //    matrix-core GEMV, int8 36 against 42 us);
 //  * the matrix-core GEMV (same weight streaming, MFMA math, rows in chunks of 16) while the
 //    groups stay within a chunk or two: OLMoE layer -4% at T=32, -13% at T=48, -11% at T=64
-//    against the GEMM, even at T=128 (+2%); int8 -7% at T=24, -2% at 48, +1% at 64.  With
+//    against the GEMM, +2% at T=128 (mean 16 rows); int8 -7% at T=24, -2% at 48, +1% at 64.  With
 //    shared experts (DeepSeek shapes) from T=8 (-4% against the VALU GEMV) to T=16 (-7%
 //    against the GEMM; -9 to -10% at T=9 and 12; +3% at T=32, where a shared expert's 32
 //    rows take two chunks); int8 -7% at T=8 and 16;
