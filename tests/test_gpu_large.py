@@ -47,3 +47,11 @@ def test_rows_buffer_past_2_pow_31_elements():
     T = WIDE.tokens[0]
     assert (T * WIDE.k + WIDE.S * T) * WIDE.d > 2 ** 31
     _check(WIDE, T)
+
+
+# K = 16384 for gate/up: both GEMVs take several rounds over K per row chunk (weights
+# reloaded per round), T = 5 on the VALU GEMV, T = 12 on the matrix-core GEMV (64-K blocks,
+# 32 per round: eight rounds)
+@pytest.mark.parametrize("T", [5, 12])
+def test_wide_rows_at_decode_sizes(T):
+    _check(WIDE, T)
