@@ -392,12 +392,19 @@ class Point:
         torch.cuda.empty_cache()
 
 
+DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2}  # moe_dtype_t
+
+
 def roofline_for(wl, T, work, kern_ms, traffic=None):
     """Roofline of the gate/up kernel: its algorithmic bytes against the HBM peak and its
     flops against the bf16 matrix peak; the bound is whichever takes longer at peak, and
     frac is that time over the measured launch time."""
-    gemm = T > 8 and wl.act == "bf16"
-    name = "grouped gate/up + SwiGLU (" + ("MFMA GEMM" if gemm else "GEMV") + ")"
+    from grouped_expert_ffn_amd import abi
+    desc = abi.make_desc(wl.d, wl.E, wl.k, wl.I, wl.S, wl.renormalize, DTYPE_CODES[wl.act],
+                         DTYPE_CODES[wl.wdt])
+    family = abi.moe_ffn_kernel(desc, T)  # the library's own choice for this layer and T
+    name = "grouped gate/up + SwiGLU (" + {abi.MOE_FFN_GEMV: "GEMV", abi.MOE_FFN_GEMV_MFMA: "matrix-core GEMV",
+                                          abi.MOE_FFN_GEMM: "MFMA GEMM"}[family] + ")"
     hbm = work["gate_up_bytes"] / (kern_ms * 1e-3) / 1e9
     mfma = work["gate_up_flops"] / (kern_ms * 1e-3) / 1e12
     common = {"kernel": name, "traffic": traffic, "bytes_per_launch": work["gate_up_bytes"],

@@ -21,10 +21,11 @@ MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
 MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_time_next_launch", "moe_status_str", "moe_last_error",
-           "moe_version")
+           "moe_forward", "moe_time_next_launch", "moe_ffn_kernel", "moe_status_str",
+           "moe_last_error", "moe_version")
 (MOE_KERNEL_RMSNORM, MOE_KERNEL_ROUTER, MOE_KERNEL_TOPK, MOE_KERNEL_PERMUTE, MOE_KERNEL_GATE_UP,
  MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE) = range(7)
+MOE_FFN_GEMV, MOE_FFN_GEMV_MFMA, MOE_FFN_GEMM = range(3)
 
 
 class MoeError(RuntimeError):
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "moe_combine": (i32, [D, i32, vp, vp, vp, vp, vp, vp]),
             "moe_forward": (i32, [D, i32, vp, vp, vp, W, vp, vp, vp, vp, vp, sz, vp]),
             "moe_time_next_launch": (i32, [i32, vp, vp]),
+            "moe_ffn_kernel": (i32, [D, i32]),
             "moe_status_str": (ctypes.c_char_p, [i32]),
             "moe_last_error": (ctypes.c_char_p, []),
             "moe_version": (i32, []),
@@ -165,6 +167,14 @@ def moe_forward(desc, T, x, w_router, router_bias, weights: ExpertWeights, resid
                              ctypes.byref(weights), _ptr(residual), _ptr(y), _ptr(topk_ids_out),
                              _ptr(topk_w_out), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_forward")
+
+
+def moe_ffn_kernel(desc: LayerDesc, T: int) -> int:
+    """The kernel family (MOE_FFN_*) the grouped FFN launches for T tokens; host-only."""
+    r = int(lib().moe_ffn_kernel(ctypes.byref(desc), T))
+    if r < 0:
+        _check(r, "moe_ffn_kernel")
+    return r
 
 
 def moe_time_next_launch(kernel: int, start_event, stop_event) -> None:

@@ -251,6 +251,19 @@ size_t moe_workspace_bytes(const moe_layer_desc_t* desc, int32_t max_tokens, int
   }
 }
 
+int32_t moe_ffn_kernel(const moe_layer_desc_t* desc, int32_t T) {
+  LayerDims L;
+  int32_t st = check_desc(desc, &L);
+  if (st != MOE_OK) return st;
+  if (T < 1) return fail(MOE_ERR_INVALID, "T = %d: the kernel choice needs at least one token", T);
+  if ((st = check_tokens(L, T)) != MOE_OK) return st;
+  switch (ffn_path(L, T)) {
+    case FfnPath::kGemv: return MOE_FFN_GEMV;
+    case FfnPath::kGemvMfma: return MOE_FFN_GEMV_MFMA;
+    default: return MOE_FFN_GEMM;
+  }
+}
+
 int32_t moe_route(const moe_layer_desc_t* desc, int32_t T, const void* x, const void* w_router,
                   const float* router_bias, const float* logits_in, float* logits_out,
                   int32_t* topk_ids, float* topk_w, void* stream) {

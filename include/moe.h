@@ -193,6 +193,19 @@ typedef enum {
  * NULL events disarm the hook.  Returns MOE_ERR_INVALID for an unknown kernel. */
 int32_t moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event);
 
+/* Which kernel family moe_grouped_ffn (and moe_forward) launches for T tokens of this layer
+ * (switchyard §02 "One launch for all experts": a weight-streaming grouped GEMV at decode
+ * sizes, a grouped GEMM beyond; here a third family sits between them):
+ *   MOE_FFN_GEMV       weight-streaming GEMV with VALU dot products (groups of a few rows)
+ *   MOE_FFN_GEMV_MFMA  the same weight streaming with matrix-core math (groups of up to a few
+ *                      dozen rows; bf16 activations, d and I multiples of 64)
+ *   MOE_FFN_GEMM       grouped matrix-core GEMM fed by an LDS ring (larger groups)
+ * All three compute the same function with fp32 accumulation; their results may differ in the
+ * last bits.  Host-only: touches no GPU.  Returns the family, or a negative moe_status_t for
+ * an invalid descriptor or T outside 1 .. the supported maximum. */
+typedef enum { MOE_FFN_GEMV = 0, MOE_FFN_GEMV_MFMA = 1, MOE_FFN_GEMM = 2 } moe_ffn_kernel_t;
+int32_t moe_ffn_kernel(const moe_layer_desc_t* desc, int32_t T);
+
 /* Name of a status code, and the detail of this thread's last failure ("" if none). */
 const char* moe_status_str(int32_t status);
 const char* moe_last_error(void);

@@ -152,3 +152,33 @@ def test_timing_hook_refusals(L):
     assert L.moe_time_next_launch(abi.MOE_KERNEL_GATE_UP, None, fake) == abi.MOE_ERR_INVALID
     # both NULL disarms, which is always valid
     assert L.moe_time_next_launch(abi.MOE_KERNEL_GATE_UP, None, None) == abi.MOE_OK
+
+
+# The kernel family per layer and T: the regime edges of the dispatch rule, host-only.
+#   OLMoE shapes (E=64, k=8, routed only): VALU GEMV up to 3 mean rows per group (T <= 24;
+#   int8 2 rows, T <= 16), matrix-core GEMV up to 8 (T <= 64; int8 6 rows, T <= 48);
+#   DeepSeek shapes (one or more shared experts): T <= 7 / 8-16 / beyond;
+#   fp32 layers always the VALU GEMV; d not a multiple of 64: no matrix-core GEMV.
+G, GM, MM = abi.MOE_FFN_GEMV, abi.MOE_FFN_GEMV_MFMA, abi.MOE_FFN_GEMM
+FFN_CASES = [
+    (dict(), [(1, G), (24, G), (25, GM), (64, GM), (65, MM), (2048, MM)]),
+    (dict(w_dtype=abi.MOE_I8), [(16, G), (17, GM), (48, GM), (49, MM)]),
+    (dict(top_k=6, d_ff=1408, n_shared=2), [(7, G), (8, GM), (16, GM), (17, MM)]),
+    (dict(top_k=6, d_ff=1408, n_shared=2, w_dtype=abi.MOE_I8), [(7, G), (8, GM), (16, GM), (17, MM)]),
+    (dict(act_dtype=abi.MOE_F32, w_dtype=abi.MOE_F32), [(1, G), (2048, G)]),
+    (dict(d_model=272, d_ff=208, n_experts=8, top_k=2, n_shared=1), [(8, G), (9, MM)]),
+    (dict(d_model=272, d_ff=208, n_experts=8, top_k=2), [(32, G), (33, MM)]),
+]
+
+
+@pytest.mark.parametrize("kw,points", FFN_CASES, ids=[str(c[0]) for c in FFN_CASES])
+def test_ffn_kernel_regimes(L, kw, points):
+    d = desc(**kw)
+    assert [(T, abi.moe_ffn_kernel(d, T)) for T, _ in points] == points
+
+
+def test_ffn_kernel_refusals(L):
+    with pytest.raises(abi.MoeError):
+        abi.moe_ffn_kernel(desc(), 0)
+    with pytest.raises(abi.MoeError):
+        abi.moe_ffn_kernel(desc(top_k=65), 8)
