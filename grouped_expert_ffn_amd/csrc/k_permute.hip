@@ -34,7 +34,12 @@ namespace {
 
 constexpr int kPermWaves = 16;
 constexpr int kMaxGroups = 256 + 8;
-constexpr int kFusedMaxRows = 2048;  // T*k limit of the fused top-k + sort kernel
+// T*k limit of the fused top-k + sort kernel.  Its one workgroup selects every token's top-k
+// in turn (16 wavefronts), so past a few hundred rows the separate top-k launch (a wavefront
+// per token over the whole chip) and the one-workgroup sort are faster: OLMoE layer -5% at
+// T=64 (512 rows), -7% at 128, -12% at 256; DeepSeek -3% at 64, -6% at 128, -12% at 256;
+// equal up to 256 rows (OLMoE T=32), where the fused launch saves a launch.
+constexpr int kFusedMaxRows = 256;
 constexpr int kSingleMaxRows = 4096;  // T*k up to which one workgroup sorts every row
 constexpr int kStageLoads = kSingleMaxRows / (kPermWaves * kWave);  // staging loads per thread
 static_assert(kFusedMaxRows <= kSingleMaxRows, "the fused kernel sorts in one workgroup");
