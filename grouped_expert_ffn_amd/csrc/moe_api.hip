@@ -271,6 +271,10 @@ int32_t moe_route(const moe_layer_desc_t* desc, int32_t T, const void* x, const 
   int32_t st = check_desc(desc, &L);
   if (st) return st;
   if ((st = check_tokens(L, T))) return st;
+  if (desc->pre_norm)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "pre_norm = 1: moe_route takes x (or logits_in) as given; only moe_forward applies "
+                "the RMSNorm, so pass the normalised input with pre_norm = 0");
   REQUIRE_PTR(topk_ids);
   REQUIRE_PTR(topk_w);
   CHECK_ALIGN(logits_out);
@@ -329,6 +333,10 @@ int32_t moe_grouped_ffn(const moe_layer_desc_t* desc, int32_t T, const void* x,
   if (st) return st;
   if ((st = check_tokens(L, T))) return st;
   if ((st = check_weights(L, weights))) return st;
+  if (desc->pre_norm)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "pre_norm = 1: moe_grouped_ffn takes x as given; only moe_forward applies the "
+                "RMSNorm, so pass the normalised input with pre_norm = 0");
   REQUIRE_PTR(x);
   REQUIRE_PTR(offsets);
   REQUIRE_PTR(perm);

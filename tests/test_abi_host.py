@@ -182,3 +182,18 @@ def test_ffn_kernel_refusals(L):
         abi.moe_ffn_kernel(desc(), 0)
     with pytest.raises(abi.MoeError):
         abi.moe_ffn_kernel(desc(top_k=65), 8)
+
+
+def test_pre_norm_is_refused_by_the_calls_that_take_x(L):
+    # the RMSNorm prologue belongs to moe_forward; the step calls take x as given, so a
+    # descriptor asking for it (with or without logits_in) is refused rather than ignored
+    d = desc(pre_norm=True)
+    w = abi.make_weights(0x1000, 0x1000, 0x1000)
+    for logits_in in (None, 0x1000):
+        with pytest.raises(abi.MoeError) as ei:
+            abi.moe_route(d, 4, 0x1000, 0x1000, None, logits_in, 0x1000, 0x1000, 0x1000, stream=0)
+        assert ei.value.status == abi.MOE_ERR_UNSUPPORTED and "pre_norm" in str(ei.value)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_grouped_ffn(d, 8, 0x1000, w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 30,
+                            stream=0)
+    assert ei.value.status == abi.MOE_ERR_UNSUPPORTED and "pre_norm" in str(ei.value)

@@ -489,3 +489,135 @@ def test_capacity_layer_equals_dense_masked_gates_and_combine():
     _, _, perm, inv = O.permute_with_capacity(ids, E, cap)
     _, rows = O.sorted_rows(x, ex, ids, perm, S, E)
     np.testing.assert_allclose(O.combine(rows, inv, w, S), y, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# gate weights of a choice made elsewhere (the weights every end-to-end
+# comparison feeds the oracle when the GPU's routing is taken as input)
+# --------------------------------------------------------------------------
+def test_gate_weights_for_equals_route_on_its_own_choice():
+    g = rng(51)
+    logits = g.standard_normal((40, 64)) * 1.5
+    for ren in (False, True):
+        ids, w = O.route(logits, 8, ren)
+        np.testing.assert_array_equal(O.gate_weights_for(logits, ids, ren), w)
+
+
+@pytest.mark.parametrize("E", [8, 64])
+def test_gate_weights_for_closed_form_on_a_chosen_set(E):
+    # logits (L, 0, ..., 0): p_0 = e^L / (e^L + E - 1), every other p_e = 1 / (e^L + E - 1)
+    L = 1.75
+    logits = np.zeros((3, E))
+    logits[:, 0] = L
+    eL = math.exp(L)
+    den = eL + E - 1
+    # token 0: the top-1 expert plus a non-top choice; token 1: the same pair in the other
+    # slot order; token 2: two experts that are not the top choice
+    ids = np.array([[0, 3], [3, 0], [3, 5]])
+    w = O.gate_weights_for(logits, ids, renormalize=False)
+    np.testing.assert_allclose(w, [[eL / den, 1 / den], [1 / den, eL / den], [1 / den, 1 / den]],
+                               rtol=1e-15)
+    wr = O.gate_weights_for(logits, ids, renormalize=True)
+    np.testing.assert_allclose(wr, [[eL / (eL + 1), 1 / (eL + 1)], [1 / (eL + 1), eL / (eL + 1)],
+                                    [0.5, 0.5]], rtol=1e-15)
+
+
+def test_gate_weights_for_rows_are_per_token():
+    # two tokens with different logits: each row of weights comes from its own token's softmax
+    logits = np.array([[2.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, -1.0]])
+    ids = np.array([[0, 1], [3, 2]])
+    w = O.gate_weights_for(logits, ids, renormalize=False)
+    d0 = math.exp(2.0) + 3
+    d1 = 3 + math.exp(-1.0)
+    np.testing.assert_allclose(w, [[math.exp(2.0) / d0, 1 / d0], [math.exp(-1.0) / d1, 1 / d1]],
+                               rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# int8 experts: which per-channel scale goes with which matrix
+# --------------------------------------------------------------------------
+def test_int8_experts_pair_each_matrix_with_its_own_scales():
+    # one nonzero int8 weight per matrix at distinct positions, and scales that differ per
+    # matrix and per channel, so that a scale taken from the wrong matrix or channel moves
+    # the value: FFN(x) = sd[m] qd * silu(sg[n] qg x[cg]) * (su[n] qu x[cu]) in output m
+    E, d, I = 2, 6, 4
+    qg = np.zeros((E, I, d), dtype=np.int8)
+    qu = np.zeros((E, I, d), dtype=np.int8)
+    qd = np.zeros((E, d, I), dtype=np.int8)
+    sg = np.zeros((E, I), dtype=np.float32)
+    su = np.zeros((E, I), dtype=np.float32)
+    sd = np.zeros((E, d), dtype=np.float32)
+    for e in range(E):
+        sg[e] = [1.0, 0.5, 0.25, 0.125][e:] + [3.0] * e
+        su[e] = 2.0 * (e + 1) + np.arange(I)
+        sd[e] = 4.0 + 0.5 * np.arange(d) + 8.0 * e
+    spec = []
+    for e in range(E):
+        n, cg, cu, m = (e + 1) % I, (2 * e + 1) % d, (3 * e + 4) % d, (5 * e + 2) % d
+        qg[e, n, cg], qu[e, n, cu], qd[e, m, n] = 7 - e, -3 - e, 5 + 2 * e
+        spec.append((n, cg, cu, m))
+    ex = O.Experts(qg, qu, qd, sg, su, sd)
+    x = np.array([0.5, -1.0, 1.5, -0.25, 0.75, 2.0])
+    for e in range(E):
+        n, cg, cu, m = spec[e]
+        wg, wu, wd = ex.get(e)
+        # each dequantised matrix holds exactly one value: its q times its own channel scale
+        assert wg[n, cg] == float(qg[e, n, cg]) * float(sg[e, n]) and np.count_nonzero(wg) == 1
+        assert wu[n, cu] == float(qu[e, n, cu]) * float(su[e, n]) and np.count_nonzero(wu) == 1
+        assert wd[m, n] == float(qd[e, m, n]) * float(sd[e, m]) and np.count_nonzero(wd) == 1
+        a = float(qg[e, n, cg]) * float(sg[e, n]) * x[cg]
+        b = float(qu[e, n, cu]) * float(su[e, n]) * x[cu]
+        ref = np.zeros(d)
+        ref[m] = float(qd[e, m, n]) * float(sd[e, m]) * silu_scalar(a) * b
+        y = O.moe_layer(x[None], ex, np.array([[e]]), np.array([[1.0]]), n_shared=0, n_experts=E)
+        np.testing.assert_allclose(y[0], ref, rtol=1e-15, atol=0)
+
+
+def test_int8_experts_of_the_quantiser_reproduce_dequantised_float_experts():
+    # an int8 layer equals the same layer given as the float64 arrays q * scale
+    import moe_synth as S
+    g = rng(52)
+    G, d, I = 3, 32, 16
+    w = (g.standard_normal((3, G, I, d)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((G, d, I)) * 0.02).astype(np.float32)
+    (qg, sg), (qu, su), (qd, sd) = S.quantize_int8_rows(w[0]), S.quantize_int8_rows(w[1]), S.quantize_int8_rows(wd)
+    ex8 = O.Experts(qg, qu, qd, sg, su, sd)
+    exf = O.Experts(qg * sg[..., None].astype(np.float64), qu * su[..., None].astype(np.float64),
+                    qd * sd[..., None].astype(np.float64))
+    x = g.standard_normal((5, d))
+    ids = np.array([[0, 2], [1, 0], [2, 1], [0, 1], [2, 0]])
+    wts = g.random((5, 2))
+    np.testing.assert_array_equal(O.moe_layer(x, ex8, ids, wts, 0, G),
+                                  O.moe_layer(x, exf, ids, wts, 0, G))
+
+
+# --------------------------------------------------------------------------
+# token and row subsets (every sampled comparison uses them)
+# --------------------------------------------------------------------------
+def test_moe_layer_token_subset_equals_rows_of_the_full_layer():
+    E, d, I, T, k, S = 6, 10, 7, 12, 2, 1
+    ex = random_experts(E + S, d, I, 53)
+    g = rng(54)
+    x = g.standard_normal((T, d))
+    ids, w = O.route(g.standard_normal((T, E)), k, True)
+    res = g.standard_normal((T, d))
+    keep = O.kept_slots(ids, E, 3)
+    assert not keep.all()
+    full = O.moe_layer(x, ex, ids, w, S, E, residual=res, keep=keep)
+    for sub in ([9, 2, 7], [11, 0], [5], [3, 3, 10, 1]):  # unsorted, non-contiguous, repeated
+        part = O.moe_layer(x, ex, ids, w, S, E, residual=res, tokens=sub, keep=keep)
+        np.testing.assert_array_equal(part, full[sub])
+
+
+def test_sorted_rows_row_subset_equals_rows_of_the_full_call():
+    E, d, I, T, k, S = 5, 8, 6, 9, 2, 2
+    ex = random_experts(E + S, d, I, 55)
+    g = rng(56)
+    x = g.standard_normal((T, d))
+    ids, _ = O.route(g.standard_normal((T, E)), k, False)
+    _, _, perm, _ = O.permute(ids, E)
+    h, rows = O.sorted_rows(x, ex, ids, perm, S, E)
+    sub = [T * k + T + 4, 3, 17, 0, T * k + 1]  # shared rows of both experts and routed rows
+    hs, rs = O.sorted_rows(x, ex, ids, perm, S, E, rows=sub)
+    np.testing.assert_array_equal(hs, h[sub])
+    np.testing.assert_array_equal(rs, rows[sub])
