@@ -21,7 +21,7 @@ MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
 MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_time_next_launch", "moe_ffn_kernel", "moe_status_str",
+           "moe_forward", "moe_forward_noalloc", "moe_time_next_launch", "moe_ffn_kernel", "moe_status_str",
            "moe_last_error", "moe_version")
 (MOE_KERNEL_RMSNORM, MOE_KERNEL_ROUTER, MOE_KERNEL_TOPK, MOE_KERNEL_PERMUTE, MOE_KERNEL_GATE_UP,
  MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE) = range(7)
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_ffn": (i32, [D, i32, vp, W, vp, vp, vp, vp, vp, sz, vp]),
             "moe_combine": (i32, [D, i32, vp, vp, vp, vp, vp, vp]),
             "moe_forward": (i32, [D, i32, vp, vp, vp, W, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_forward_noalloc": (i32, [D, i32, vp, vp, vp, W, vp, vp, vp, vp, vp]),
             "moe_time_next_launch": (i32, [i32, vp, vp]),
             "moe_ffn_kernel": (i32, [D, i32]),
             "moe_status_str": (ctypes.c_char_p, [i32]),
@@ -167,6 +168,14 @@ def moe_forward(desc, T, x, w_router, router_bias, weights: ExpertWeights, resid
                              ctypes.byref(weights), _ptr(residual), _ptr(y), _ptr(topk_ids_out),
                              _ptr(topk_w_out), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_noalloc(desc, T, x, w_router, router_bias, weights: ExpertWeights, residual, y,
+                        topk_ids_out, topk_w_out, stream=None) -> None:
+    _check(lib().moe_forward_noalloc(ctypes.byref(desc), T, _ptr(x), _ptr(w_router),
+                                     _ptr(router_bias), ctypes.byref(weights), _ptr(residual),
+                                     _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out),
+                                     _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_ffn_kernel(desc: LayerDesc, T: int) -> int:

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -207,6 +208,61 @@ hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipSt
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Scratch memory of moe_forward_noalloc, for callers that cannot allocate.  One copy per GPU:
+// the array is part of the library's device code object, so each device the library runs on
+// holds its own copy from the code object's load until the process ends.  In host code the
+// array's name is only a host-side stand-in; its device address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is ever handed to kernels.  Every call on a device shares the device's copy, which
+// keeps the last call's contents; nothing in it has to start at zero (each kernel writes
+// what a later one reads).
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)128 << 20;  // 128 MiB: the OLMoE-shaped layer up
+                                                      // to about 2,700 tokens
+__attribute__((used)) static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device ordinal
+
+// The device `stream` belongs to, and that device's address of `scratch` (looked up on the
+// first call for the device, with the device made current for the lookup).
+int32_t scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return device_fail(e, "hipStreamGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device ordinal %d beyond the %d this library tracks", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return device_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return device_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return device_fail(e2, "hipSetDevice");
+    }
+    if (e != hipSuccess) return device_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u)) return fail(MOE_ERR_DEVICE, "scratch address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+int32_t forward_impl(const moe_layer_desc_t* desc, int32_t T, const void* x, const void* w_router,
+                     const float* router_bias, const moe_expert_weights_t* weights,
+                     const void* residual, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, void* stream, bool use_scratch);
+
+}  // namespace
+
 }  // namespace moe
 
 using namespace moe;
@@ -375,6 +431,27 @@ int32_t moe_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, cons
                     const float* router_bias, const moe_expert_weights_t* weights, const void* residual,
                     void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                     void* stream) {
+  return forward_impl(desc, T, x, w_router, router_bias, weights, residual, y, topk_ids_out, topk_w_out,
+                      ws, ws_bytes, stream, /*use_scratch=*/false);
+}
+
+int32_t moe_forward_noalloc(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                            const void* w_router, const float* router_bias,
+                            const moe_expert_weights_t* weights, const void* residual, void* y,
+                            int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  return forward_impl(desc, T, x, w_router, router_bias, weights, residual, y, topk_ids_out, topk_w_out,
+                      nullptr, 0, stream, /*use_scratch=*/true);
+}
+
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+int32_t forward_impl(const moe_layer_desc_t* desc, int32_t T, const void* x, const void* w_router,
+                     const float* router_bias, const moe_expert_weights_t* weights,
+                     const void* residual, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, void* stream, bool use_scratch) {
   LayerDims L;
   int32_t st = check_desc(desc, &L);
   if (st) return st;
@@ -383,12 +460,22 @@ int32_t moe_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, cons
   REQUIRE_PTR(x);
   REQUIRE_PTR(w_router);
   REQUIRE_PTR(y);
-  REQUIRE_PTR(ws);
+  if (!use_scratch) REQUIRE_PTR(ws);
   CHECK_ALIGN(router_bias);
   CHECK_ALIGN(residual);
   CHECK_ALIGN(topk_ids_out);
   CHECK_ALIGN(topk_w_out);
   const size_t need = moe_workspace_bytes(desc, T, MOE_WS_FORWARD);
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(MOE_ERR_WORKSPACE,
+                  "T = %d needs %zu bytes of workspace; the library's static scratch holds %zu "
+                  "(use moe_forward with a caller workspace)",
+                  T, need, kScratchBytes);
+    if (T == 0) return ok();
+    if ((st = scratch_for_stream((hipStream_t)stream, &ws))) return st;
+    ws_bytes = kScratchBytes;
+  }
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, need);
   if (T == 0) return ok();
 
@@ -437,4 +524,5 @@ int32_t moe_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, cons
   return ok();
 }
 
-}  // extern "C"
+}  // namespace
+}  // namespace moe

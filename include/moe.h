@@ -34,8 +34,8 @@
  *  - T == 0 is a valid no-op.
  *  - Results are deterministic: identical inputs give bit-identical outputs on every run
  *    (no floating-point atomics anywhere).
- *  - The library keeps no state between calls; calls that run concurrently need
- *    distinct outputs and workspaces.
+ *  - The library keeps no state between calls (apart from the static scratch array of
+ *    moe_forward_noalloc); calls that run concurrently need distinct outputs and workspaces.
  *  - Every pointer must be 16-byte aligned.
  *
  * Matrices are row-major [out, in] with `in` contiguous (the layout of a PyTorch Linear
@@ -110,7 +110,9 @@ size_t moe_workspace_bytes(const moe_layer_desc_t* desc, int32_t max_tokens, int
  *   as they are (x, w_router and router_bias are then ignored and may be NULL).
  * logits_out [T,E] fp32: receives the logits; required when logits_in is NULL, may be NULL
  *   otherwise.
- * topk_ids [T,k] int32, topk_w [T,k] fp32: outputs. */
+ * topk_ids [T,k] int32, topk_w [T,k] fp32: outputs.
+ * desc->pre_norm must be 0 (MOE_ERR_UNSUPPORTED otherwise): the RMSNorm prologue is
+ * moe_forward's; the step calls take x as given. */
 int32_t moe_route(const moe_layer_desc_t* desc, int32_t T, const void* x, const void* w_router,
                   const float* router_bias, const float* logits_in, float* logits_out,
                   int32_t* topk_ids, float* topk_w, void* stream);
@@ -143,7 +145,8 @@ int32_t moe_permute(const moe_layer_desc_t* desc, int32_t T, const int32_t* topk
  * applied to the fp32 accumulator.  Accumulation is fp32; h is rounded to act_dtype.
  * x [T,d]; offsets, perm as written by moe_permute; plan as written by that same
  * moe_permute call; rows [T*k + S*T, d] act_dtype (output: the rows of dropped slots are
- * left unwritten); ws >= moe_workspace_bytes(desc, T, MOE_WS_GROUPED_FFN). */
+ * left unwritten); ws >= moe_workspace_bytes(desc, T, MOE_WS_GROUPED_FFN).
+ * desc->pre_norm must be 0 (MOE_ERR_UNSUPPORTED otherwise), as for moe_route. */
 int32_t moe_grouped_ffn(const moe_layer_desc_t* desc, int32_t T, const void* x,
                         const moe_expert_weights_t* weights, const int32_t* offsets,
                         const int32_t* perm, const void* plan, void* rows, void* ws,
@@ -161,7 +164,10 @@ int32_t moe_combine(const moe_layer_desc_t* desc, int32_t T, const void* rows,
                     const int32_t* inv_perm, const float* topk_w, const void* residual,
                     void* y, void* stream);
 
-/* The whole layer: [RMSNorm] -> route -> permute -> grouped FFN -> combine.
+/* The whole layer: [RMSNorm] -> route -> permute -> grouped FFN -> combine (the layer as the
+ * switchyard page draws it: tokens, router top-k, experts, combine, §02 "Kernels and
+ * dispatch"; the RMSNorm prologue and residual serve a stack of such layers, one per
+ * transformer block).
  *   y = residual + MoE(pre_norm ? x / sqrt(mean(x^2) + eps) : x)
  * The normalised input is rounded to act_dtype and fed to both router and experts.
  * x [T,d]; residual [T,d] or NULL (may alias x or y); y [T,d] (may alias x).
@@ -171,6 +177,22 @@ int32_t moe_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, cons
                     const float* router_bias, const moe_expert_weights_t* weights,
                     const void* residual, void* y, int32_t* topk_ids_out, float* topk_w_out,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops that forbid allocation): the workspace is a
+ * static scratch array inside the library's device code, 128 MiB, one copy per GPU, held
+ * from the library's first use on that GPU until the process ends.  Arguments, results and
+ * determinism are those of moe_forward (same kernels, bit-identical outputs); the call
+ * allocates and frees nothing.  A layer and T whose moe_workspace_bytes(desc, T,
+ * MOE_WS_FORWARD) exceeds 128 MiB is refused with MOE_ERR_WORKSPACE (about 2,700 tokens for
+ * an OLMoE-shaped layer, 2,400 for a DeepSeek-MoE-shaped one).  Every call on one GPU uses
+ * that GPU's one scratch array: calls that overlap in time on the same GPU (different
+ * streams, or threads) race and give undefined results; serialise them.  The device is the
+ * one `stream` belongs to. */
+int32_t moe_forward_noalloc(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                            const void* w_router, const float* router_bias,
+                            const moe_expert_weights_t* weights, const void* residual, void* y,
+                            int32_t* topk_ids_out, float* topk_w_out, void* stream);
 
 /* Kernels of the path, for moe_time_next_launch. */
 typedef enum {

@@ -197,3 +197,17 @@ def test_pre_norm_is_refused_by_the_calls_that_take_x(L):
         abi.moe_grouped_ffn(d, 8, 0x1000, w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 30,
                             stream=0)
     assert ei.value.status == abi.MOE_ERR_UNSUPPORTED and "pre_norm" in str(ei.value)
+
+
+def test_noalloc_refuses_a_layer_beyond_its_scratch_and_takes_zero_tokens(L):
+    # both decided on the host: no GPU is touched
+    d = desc()
+    w = abi.make_weights(0x1000, 0x1000, 0x1000)
+    assert abi.moe_workspace_bytes(d, 4096, abi.MOE_WS_FORWARD) > 128 << 20
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_forward_noalloc(d, 4096, 0x1000, 0x1000, None, w, None, 0x1000, None, None, stream=0)
+    assert ei.value.status == abi.MOE_ERR_WORKSPACE and "scratch" in str(ei.value)
+    abi.moe_forward_noalloc(d, 0, 0x1000, 0x1000, None, w, None, 0x1000, None, None, stream=0)
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_forward_noalloc(d, 4, None, 0x1000, None, w, None, 0x1000, None, None, stream=0)
+    assert ei.value.status == abi.MOE_ERR_INVALID
