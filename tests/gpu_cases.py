@@ -3,6 +3,9 @@ compare with the fp64 oracle."""
 from __future__ import annotations
 
 import functools
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -143,3 +146,80 @@ def run_steps(gl: GpuLayer, x_dev, T: int, logits_in=None):
     moe_combine(d, T, out["rows"], out["inv_perm"], out["w"], None, out["y"])
     t.cuda.synchronize()
     return out
+
+
+# ----------------------------------------------------------------------------------------
+# the oracle over many rows or tokens: contiguous chunks in threads (NumPy's matrix-vector
+# products release the GIL), each chunk an ordinary oracle call
+# ----------------------------------------------------------------------------------------
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _chunks(items, n):
+    items = list(items)
+    step = max(1, math.ceil(len(items) / n))
+    return [items[i:i + step] for i in range(0, len(items), step)]
+
+
+def oracle_sorted_rows(x, experts, ids, perm, n_shared, n_experts, rows):
+    """O.sorted_rows over `rows`, split across threads; returns the expert outputs."""
+    parts = _chunks(rows, 4 * _threads())
+    with ThreadPoolExecutor(_threads()) as ex:
+        outs = list(ex.map(lambda r: O.sorted_rows(x, experts, ids, perm, n_shared, n_experts,
+                                                   rows=r)[1], parts))
+    return np.concatenate(outs)
+
+
+def oracle_layer(x, experts, ids, w, n_shared, n_experts, tokens, residual=None):
+    """O.moe_layer over `tokens`, split across threads."""
+    parts = _chunks(tokens, 4 * _threads())
+    with ThreadPoolExecutor(_threads()) as ex:
+        outs = list(ex.map(lambda tk: O.moe_layer(x, experts, ids, w, n_shared, n_experts,
+                                                  residual=residual, tokens=tk), parts))
+    return np.concatenate(outs)
+
+
+# ----------------------------------------------------------------------------------------
+# gate weights: the bound of the GPU's fp32 softmax against the oracle on the same logits
+# ----------------------------------------------------------------------------------------
+U = 2.0 ** -24  # unit roundoff of fp32
+
+
+def gate_weight_rtol(logits32: np.ndarray, E: int) -> np.ndarray:
+    """Per-token relative bound of a gate weight computed in fp32 as
+    expf(l - m) / sum_e expf(l_e - m), against the exact value on the same fp32 logits.
+
+    First-order terms: the subtraction l - m rounds with relative error u, i.e. an absolute
+    error |l - m| u in the exponent (at most the token's logit spread s); expf is taken to be
+    within 2 ulp (4u); the denominator repeats both for each of its terms and adds the
+    rounding of its summation tree (depth 6 over the wavefront, plus 3 sequential additions
+    in a lane when E > 64); the division adds u.  Sum:
+    (s + 4) u + (s + 4 + depth) u + u = (2 s + 9 + depth) u.  The renormalising division by
+    the sum of the k chosen terms has the same form with a shallower tree, so the bound holds
+    for it as well."""
+    lg = np.asarray(logits32, dtype=np.float64)
+    fin = np.where(np.isfinite(lg), lg, np.nan)
+    spread = np.nanmax(fin, axis=1) - np.nanmin(fin, axis=1)
+    depth = 6 + (3 if E > 64 else 0)
+    return (2.0 * spread + 9 + depth) * U
+
+
+def assert_gate_weights(got_w, ref_w, logits32, E, renorm, k, rows=None):
+    """GPU gate weights against the oracle's (computed on the same fp32 logits): within the
+    per-token bound above; with renormalisation the k weights of a token sum to 1 within
+    k u (each of the k quotients rounds once, the sum of k positive terms at most k - 1 times)."""
+    got = np.asarray(got_w, dtype=np.float64)
+    ref = np.asarray(ref_w, dtype=np.float64)
+    rt = gate_weight_rtol(logits32, E)
+    sel = np.arange(got.shape[0]) if rows is None else np.asarray(rows)
+    err = np.abs(got[sel] - ref[sel]) / np.abs(ref[sel])
+    assert np.all(err <= rt[sel, None]), \
+        f"gate weight off by {np.max(err / rt[sel, None]):.2f}x its bound"
+    if renorm:
+        dev = np.abs(got[sel].sum(1) - 1.0)
+        assert np.all(dev <= k * U * (1 + 1e-6)), f"renormalised sum off by {dev.max():.3e}"
