@@ -14,9 +14,10 @@
 // index: the sort is stable and its result unique.
 //
 // Past kSingleMaxRows rows the sort is spread over workgroups of kPermChunk rows each: a
-// first kernel writes every chunk's expert histogram, and the sort kernel then runs once per
-// chunk, taking its chunk's base for each expert from the histograms of the chunks before it
-// (the same offsets the one-workgroup kernel computes, so the result is identical).
+// first kernel writes every chunk's expert histogram, a scan turns the histograms into each
+// chunk's per-expert base (the rows of that expert in the chunks before it) and the expert
+// totals, and the sort kernel then runs once per chunk (the same offsets the one-workgroup
+// kernel computes, so the result is identical).
 //
 // With a capacity limit C, a row whose place in its expert's segment is C or later is
 // dropped (inv_perm = -1): the segment keeps ascending flat order, so these are the pairs
@@ -156,15 +157,10 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
       run += c;
     }
     if (multi) {
+      // this chunk's base for each expert and the expert totals (k_perm_scan)
       const int nb = (N + kPermChunk - 1) / kPermChunk;
-      int before = 0, total = 0;
-      for (int b = 0; b < nb; ++b) {
-        const int c = chunk_hist[(size_t)b * E + e];
-        before += b < (int)blockIdx.x ? c : 0;
-        total += c;
-      }
-      pre[e] = before;
-      cnt[e] = total;
+      pre[e] = chunk_hist[(size_t)blockIdx.x * E + e];
+      cnt[e] = chunk_hist[(size_t)nb * E + e];
     } else {
       pre[e] = 0;
       cnt[e] = run;
@@ -305,6 +301,20 @@ __global__ __launch_bounds__(1024) void k_perm_hist(int N, int E, const int32_t*
   }
 }
 
+// Exclusive scan of the chunk histograms over chunks, in place, one expert per thread; the
+// expert totals go after the last chunk.  grid: ceil(E / 256); block 256
+__global__ __launch_bounds__(256) void k_perm_scan(int nb, int E, int32_t* __restrict__ chunk_hist) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  int run = 0;
+  for (int b = 0; b < nb; ++b) {
+    const int c = chunk_hist[(size_t)b * E + e];
+    chunk_hist[(size_t)b * E + e] = run;
+    run += c;
+  }
+  chunk_hist[(size_t)nb * E + e] = run;
+}
+
 }  // namespace
 
 hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t* counts,
@@ -316,12 +326,13 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
     return launch(MOE_KERNEL_PERMUTE, k_permute<false>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m,
                   nullptr, 0, nullptr, idsm, counts, offsets, perm, inv_perm, plan, nullptr,
                   capacity_rows(L, T));
-  // two launches: the timer records its start before the first and its stop after the last
+  // three launches: the timer records its start before the first and its stop after the last
   // launch made while it is alive
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
   int32_t* chunk_hist = plan + plan_hist_offset(T, L.k, L.E, L.S);
   const int nb = (N + kPermChunk - 1) / kPermChunk;
   k_perm_hist<<<nb, 1024, 0, s>>>(N, L.E, ids, chunk_hist);
+  k_perm_scan<<<(L.E + 255) / 256, 256, 0, s>>>(nb, L.E, chunk_hist);
   k_permute<false><<<nb, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
                                        offsets, perm, inv_perm, plan, chunk_hist,
                                        capacity_rows(L, T));

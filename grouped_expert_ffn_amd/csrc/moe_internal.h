@@ -124,6 +124,7 @@ __device__ __forceinline__ float wave_max_u(float v) {
 //   [4 .. 4+E+S)            touched group ids, ascending (routed first, then shared)
 //   [4+E+S .. + 2*max_tiles) tile list: (group, first row within the group)
 //   then, for the multi-workgroup sort, one expert histogram per chunk of kPermChunk rows
+//   (turned in place into each chunk's per-expert base by a scan), then the E expert totals
 constexpr int kPlanHeader = 4;
 constexpr int kMinTileM = 16;
 constexpr int kPermChunk = 1024;  // rows per workgroup of the multi-workgroup sort
@@ -136,7 +137,7 @@ inline size_t plan_hist_offset(int T, int k, int E, int S) {
 }
 inline size_t plan_words(int T, int k, int E, int S) {
   const size_t chunks = ((size_t)T * k + kPermChunk - 1) / kPermChunk;
-  return plan_hist_offset(T, k, E, S) + chunks * (size_t)E;
+  return plan_hist_offset(T, k, E, S) + (chunks + 1) * (size_t)E;
 }
 
 // -------------------------------------------------------------------------------------
