@@ -7,10 +7,11 @@ and inputs are already resident in HBM.  The headline workload is the
 OLMoE-shaped decode layer (d=2048, E=64, k=8, I=1024, bf16) at T=8 tokens.
 
 Before a point is timed its output must be finite and bit-identical over two
-runs.  Agreement with the fp64 CPU oracle is what the GPU test suite checks;
-here the CPU-baseline leg, which runs the oracle on a sample of the headline
-tokens anyway, also compares its outputs with the GPU's for those tokens and
-withholds the JSON line if they disagree.
+runs, and a few of its tokens must agree with the fp64 CPU oracle (routing up
+to pre-registered near-ties, outputs within the parity tolerance); a point that
+fails is refused and no JSON line is printed.  The CPU-baseline leg runs the
+oracle over worker processes on the headline tokens and further tokens of the
+same workload, and compares its outputs with the GPU's for the headline tokens.
 
 The expert weights are replicated ``--copies`` times and the steps rotate over
 the copies, so the 256 MiB Infinity Cache cannot serve the weights of the next
@@ -429,6 +430,7 @@ def measure(wl, T, steps, warmup, copies, extras=False):
     from grouped_expert_ffn_amd import abi
     pt = Point(wl, T, copies)
     ids = pt.sanity_gate()
+    gate = oracle_gate(wl, pt.host, pt.x_host, pt.y_host, ids, gate_tokens(T), what=f"{wl.name} T={T}")
     n_touched = int(np.count_nonzero(np.bincount(ids.ravel(), minlength=wl.E)))
     work = layer_work(wl, T, n_touched)
     if warmup is None:
@@ -447,6 +449,7 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         "gate_up_hbm_frac": round(work["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "down_hbm_frac": round(work["down_bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "touched_experts": n_touched,
+        "oracle_gate": gate,
     }
     if T > 8 and wl.act == "bf16":
         res["gate_up_mfma_frac"] = round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
@@ -455,6 +458,10 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         res["step_ms_percentiles"] = step_percentiles(pt.step, steps)
         res["graph_ms_per_layer"] = round(pt.graph_ms(max(4, steps // copies)), 5)
     roof = roofline_for(wl, T, work, gu_ms)
+    # the whole layer (every launch of the step) against the same HBM peak, beside the one
+    # kernel's fraction: at small T the fixed cost of the other launches is what separates them
+    roof["layer_hbm_frac"] = hbm
+    roof["layer_ms"] = round(ms, 5)
     checked = (pt.x_host, pt.y_host, pt.ids_host)
     pt.free()
     return res, roof, ms, wall, work, checked
@@ -490,6 +497,8 @@ class Stack:
         for layer in range(wl.n_layers):
             h = S.make_layer(wl, layer)
             self.layers.append(DeviceLayer(self.desc, h.w_router, h.bias, h.w_gate, h.w_up, h.w_down))
+            if layer == 0:
+                self.host0 = h  # for the oracle gate
             del h
         self.x0 = to_device(self.x_host)
         self.buf = [torch.empty_like(self.x0), torch.empty_like(self.x0)]
@@ -523,13 +532,18 @@ class Stack:
             outs.append(self.buf[0].clone())
         if not (bool(torch.isfinite(outs[0].float()).all()) and torch.equal(outs[0], outs[1])):
             raise SystemExit("stack layer 0: output not finite or not deterministic; refusing to time")
-        counts = np.bincount(self.ids.cpu().numpy().ravel(), minlength=wl.E)
+        from grouped_expert_ffn_amd import from_device
+        ids = self.ids.cpu().numpy()
+        self.gate = oracle_gate(wl, self.host0, self.x_host, from_device(outs[0]), ids, gate_tokens(T),
+                                residual=self.x_host, what="stack layer 0")
+        counts = np.bincount(ids.ravel(), minlength=wl.E)
         self.skew0 = float(counts.max() / (T * wl.k / wl.E))
 
     def free(self):
         import torch
         self.layers.clear()
         self.args.clear()
+        self.host0 = None
         torch.cuda.empty_cache()
 
 
@@ -553,6 +567,7 @@ def measure_stack(wl, steps):
         "gate_up_mfma_frac": round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "down_mfma_frac": round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "busiest_over_mean_layer0": round(st.skew0, 3),
+        "oracle_gate_layer0": st.gate,
     }
     st.free()
     return res
@@ -580,6 +595,7 @@ def measure_capacity(wl, T, cf, steps, copies):
     pt = Point(wl, T, copies, cf=cf)
     ids = pt.sanity_gate()
     cap, dropped = drop_stats(ids, wl.E, cf)
+    gate = capacity_gate(wl, pt, ids, cf, dropped)
     warm_up(pt.step, copies)
     ms, _ = time_steps(pt.step, steps, 0)
     pt.free()
@@ -588,60 +604,192 @@ def measure_capacity(wl, T, cf, steps, copies):
             "ms_per_layer": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
             "dropped_pairs_frac": round(float(dropped.mean()), 4),
             "tokens_with_a_drop_frac": round(float(dropped.any(axis=1).mean()), 4),
-            "busiest_over_mean": round(float(counts.max() / (T * wl.k / wl.E)), 3)}
+            "busiest_over_mean": round(float(counts.max() / (T * wl.k / wl.E)), 3),
+            "oracle_gate": gate}
 
 
-# ------------------------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands
-# ------------------------------------------------------------------------------------------
-def cpu_baseline(wl, T, budget_s, checked):
-    """The fp64 oracle as it stands, on a bounded sample of the same workload.  The outputs it
-    produces for the headline tokens are also compared with the GPU's (`checked`: tokens,
-    output bits and routing of the run the sanity gate kept), wherever the oracle picked the
-    same experts; a disagreement withholds the bench line."""
+def capacity_gate(wl, pt, ids, cf, dropped):
+    """The oracle check of a capacity point: sampled tokens, among them tokens that lost a
+    slot, with the dropped slots left out of the oracle's sum."""
     import numpy as np
 
     from oracle import moe_oracle as O
-    host = host_layer(wl)
-    x_host, y_gpu, ids_gpu = checked
+    T = pt.T
+    lost = np.nonzero(dropped.any(axis=1))[0]
+    tokens = sorted(set(gate_tokens(T)) | set(lost[:2].tolist()))
+    xs, _ = layer_input(wl, pt.x_host[tokens])
+    logits = O.router_logits(xs, pt.host.w_router, pt.host.bias)
+    ids_g = ids[tokens]
+    w = O.gate_weights_for(logits, ids_g, wl.renormalize)
+    keep = O.kept_slots(ids, wl.E, O.capacity(cf, T, wl.k, wl.E))[tokens]
+    ref = O.moe_layer(xs, O.Experts.from_layer(pt.host), ids_g, w, wl.S, wl.E, keep=keep)
+    got = O.widen(pt.y_host[tokens])
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    if not (rel <= 1e-2 and mx <= 2e-2):
+        raise SystemExit(f"{wl.name} T={T} cf={cf}: oracle disagrees (rel-L2 {rel:.3e}, "
+                         f"max-abs/max {mx:.3e}); refusing to time")
+    return {"tokens": len(tokens), "rel_l2": float(f"{rel:.3e}"), "max_abs_over_max": float(f"{mx:.3e}")}
+
+
+# ------------------------------------------------------------------------------------------
+# parity gate of every timed point: sampled tokens against the fp64 oracle
+# ------------------------------------------------------------------------------------------
+TIE_DELTA = 1e-4        # pre-registered routing tie margin (fp64 logits)
+TIE_DELTA_NORM = 1e-3   # the router input is a bf16 rounding of an fp32 RMSNorm
+
+
+def layer_input(wl, xs):
+    """What the router and the experts see (the RMSNorm of the stacked workload, stored in the
+    activation type), and the tie margin that goes with it."""
+    from oracle import moe_oracle as O
+    if not wl.pre_norm:
+        return xs, TIE_DELTA
+    xn = O.stack_layer_input(xs, wl.norm_eps) if wl.act == "bf16" else O.rmsnorm(xs, wl.norm_eps)
+    return xn, TIE_DELTA_NORM
+
+
+def oracle_gate(wl, host, x_host, y_bits, ids_gpu, tokens, residual=None, what=""):
+    """Refuse to time a point whose sampled tokens disagree with the oracle: a routing choice
+    may differ from the oracle's only on a pre-registered near-tie, and the layer output,
+    computed by the oracle for the GPU's own choice, must be within rel-L2 1e-2 (1e-5 for
+    fp32) and max-abs 2e-2 * max|y|.  `x_host` is the layer input as the router sees it."""
+    import numpy as np
+
+    from oracle import moe_oracle as O
+    tokens = list(tokens)
+    xs, delta = layer_input(wl, x_host[tokens])
+    logits = O.router_logits(xs, host.w_router, host.bias)
+    ids_o, _ = O.route(logits, wl.k, False)
+    ids_g = ids_gpu[tokens]
+    for i in range(len(tokens)):
+        if list(ids_g[i]) != list(ids_o[i]):
+            srt = np.sort(logits[i])[::-1]
+            margin = srt[wl.k - 1] - srt[wl.k] if wl.k < wl.E else np.inf
+            gaps = np.abs(np.diff(srt[:wl.k + 1]))
+            if not (margin < delta or (len(gaps) and np.min(gaps) < delta)):
+                raise SystemExit(f"{what}: token {tokens[i]} routed {list(ids_g[i])}, oracle "
+                                 f"{list(ids_o[i])} (margin {margin:.2e}); refusing to time")
+    w = O.gate_weights_for(logits, ids_g, wl.renormalize)
+    res = None if residual is None else O.widen(residual[tokens])
+    ref = O.moe_layer(xs, O.Experts.from_layer(host), ids_g, w, wl.S, wl.E, residual=res)
+    got = O.widen(y_bits[tokens])
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300))
+    lim = 1e-5 if wl.act == "f32" else 1e-2
+    if not (rel <= lim and mx <= 2e-2):
+        raise SystemExit(f"{what}: oracle disagrees on tokens {tokens}: rel-L2 {rel:.3e}, "
+                         f"max-abs/max {mx:.3e}; refusing to time")
+    return {"tokens": len(tokens), "rel_l2": float(f"{rel:.3e}"), "max_abs_over_max": float(f"{mx:.3e}")}
+
+
+def gate_tokens(T, n=3):
+    """A few tokens spread over the batch (first, middle, last)."""
+    return sorted({0, T // 2, T - 1})[:n]
+
+
+# ------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, in worker processes over distinct tokens
+# ------------------------------------------------------------------------------------------
+def cpu_workers() -> int:
+    """Worker processes for the oracle: the host cores this process may use, at most the
+    thread budget the environment sets (OMP_NUM_THREADS) and at most 16."""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, min(16, n))
+
+
+def _oracle_worker(name, head_T, n_extra, lo, hi, budget_s, barrier, out_q):
+    """One worker of the CPU baseline: tokens [lo, hi) of (the headline tokens, then n_extra
+    further tokens of the same workload), one token at a time through the oracle, until done
+    or out of time.  Weights are widened once per expert (the oracle's lazy cache)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        cores = 1
-    done, passes = 0, 0
-    first_pass = []  # (token, oracle ids, oracle output) of the first pass, compared afterwards
+        pass
+    import numpy as np
+
+    import moe_synth as S
+    from oracle import moe_oracle as O
+    wl = S.WORKLOADS[name]
+    host = S.make_layer(wl, 0, 0, threads=1)
+    xs = np.concatenate([S.make_tokens(wl, head_T), S.make_tokens(wl, n_extra, seed=1)])
+    ex = O.Experts.from_layer(host)
+    barrier.wait()
     t0 = time.perf_counter()
-    while True:
-        ex = O.Experts.from_layer(host)  # every pass widens the stored weights again
-        for t in range(T):
-            xt = x_host[t:t + 1]
-            logits, ids, w = O.full_route(xt, host.w_router, host.bias, wl.k, wl.renormalize)
-            y = O.moe_layer(xt, ex, ids, w, wl.S, wl.E)
-            if passes == 0:
-                first_pass.append((t, ids[0], y[0]))
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        passes += 1
-        if time.perf_counter() - t0 > budget_s * 0.66 or done >= 64 * T:
+    done, head = 0, []
+    for t in range(lo, hi):
+        xt = xs[t:t + 1]
+        _, ids, w = O.full_route(xt, host.w_router, host.bias, wl.k, wl.renormalize)
+        y = O.moe_layer(xt, ex, ids, w, wl.S, wl.E)
+        if t < head_T:
+            head.append((t, ids[0], y[0]))
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
             break
-    el = time.perf_counter() - t0
-    out = {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-           "sample": f"{done} tokens of {wl.name} T={T} ({passes} pass(es), fp64 per-token "
-                     f"per-expert loop incl. weight widening), {el:.1f} s"}
-    same = [(t, y) for t, ids, y in first_pass if np.array_equal(ids, ids_gpu[t])]
-    if same:
-        ref = np.array([y for _, y in same])
-        got = O.widen(y_gpu[[t for t, _ in same]])
-        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-        mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
-        out["parity"] = {"tokens": len(first_pass), "same_routing": len(same),
-                         "rel_l2": float(f"{rel:.3e}"), "max_abs_over_max": float(f"{mx:.3e}")}
-        lim = 1e-5 if wl.act == "f32" else 1e-2
-        if not (rel <= lim and mx <= 2e-2):
-            raise SystemExit(f"oracle disagrees with the GPU on {wl.name} T={T}: rel-L2 {rel:.3e}, "
-                             f"max-abs/max {mx:.3e}; no bench line")
+    out_q.put((done, time.perf_counter() - t0, head))
+
+
+def cpu_baseline(wl, T, budget_s, checked):
+    """The fp64 oracle as it stands, spread over worker processes on distinct tokens of the
+    same workload (the headline tokens first), for about `budget_s` seconds.  Its outputs for
+    the headline tokens are compared with the GPU's (`checked`: tokens, output bits and routing
+    of the run the sanity gate kept) wherever the oracle picked the same experts; none in
+    common, or a disagreement, withholds the bench line."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    from oracle import moe_oracle as O
+    x_host, y_gpu, ids_gpu = checked
+    n = cpu_workers()
+    per = 48                                  # tokens per worker at most (the bounded sample)
+    total = n * per
+    n_extra = max(0, total - T)
+    ctx = mp.get_context("spawn")             # fresh interpreters: no GPU state is inherited
+    barrier, q = ctx.Barrier(n + 1), ctx.Queue()
+    bounds = [(i * total // n, (i + 1) * total // n) for i in range(n)]
+    procs = [ctx.Process(target=_oracle_worker, args=(wl.name, T, n_extra, lo, hi, budget_s, barrier, q))
+             for lo, hi in bounds]
+    for p in procs:
+        p.start()
+    try:
+        barrier.wait(timeout=600)             # every worker has its weights and tokens
+        t0 = time.perf_counter()
+        results = [q.get(timeout=budget_s + 600) for _ in procs]
+        wall = time.perf_counter() - t0
+    except Exception as e:                    # a worker died or stalled: no baseline
+        for p in procs:
+            p.kill()
+        raise SystemExit(f"CPU baseline workers failed ({type(e).__name__}); no bench line")
+    for p in procs:
+        p.join()
+    done = sum(r[0] for r in results)
+    head = sorted([h for r in results for h in r[2]], key=lambda h: h[0])
+    out = {"value": round(done / wall, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
+           "sample": f"{done} distinct tokens of {wl.name} (the {T} headline tokens, then further "
+                     f"seeded tokens), {n} worker processes, fp64 per-token per-expert loop "
+                     f"incl. weight widening, {wall:.1f} s"}
+    same = [(t, y) for t, ids, y in head if np.array_equal(ids, ids_gpu[t])]
+    if not same:
+        raise SystemExit(f"oracle and GPU share no routing on the {T} headline tokens; no bench line")
+    ref = np.array([y for _, y in same])
+    got = O.widen(y_gpu[[t for t, _ in same]])
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    out["parity"] = {"tokens": len(head), "same_routing": len(same),
+                     "rel_l2": float(f"{rel:.3e}"), "max_abs_over_max": float(f"{mx:.3e}")}
+    lim = 1e-5 if wl.act == "f32" else 1e-2
+    if not (rel <= lim and mx <= 2e-2):
+        raise SystemExit(f"oracle disagrees with the GPU on {wl.name} T={T}: rel-L2 {rel:.3e}, "
+                         f"max-abs/max {mx:.3e}; no bench line")
     return out
 
 
