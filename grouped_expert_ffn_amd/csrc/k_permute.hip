@@ -27,6 +27,7 @@
 // ascending list of groups that have rows (touched routed experts, then the shared experts)
 // and, for the MFMA path, the list of (group, first row) M-tiles.
 #include "moe_internal.h"
+#include "small_sort.h"
 #include "topk.h"
 
 namespace moe {
@@ -34,7 +35,6 @@ namespace moe {
 namespace {
 
 constexpr int kPermWaves = 16;
-constexpr int kMaxGroups = 256 + 8;
 // T*k limit of the fused top-k + sort kernel.  Its one workgroup selects every token's top-k
 // in turn (16 wavefronts), so past a few hundred rows the separate top-k launch (a wavefront
 // per token over the whole chip) and the one-workgroup sort are faster: OLMoE layer -5% at
@@ -45,31 +45,6 @@ constexpr int kSingleMaxRows = 4096;  // T*k up to which one workgroup sorts eve
 constexpr int kStageLoads = kSingleMaxRows / (kPermWaves * kWave);  // staging loads per thread
 static_assert(kFusedMaxRows <= kSingleMaxRows, "the fused kernel sorts in one workgroup");
 static_assert(kPermChunk == kPermWaves * kWave, "one 64-row step per wavefront and chunk");
-
-// Inclusive prefix sum over the wavefront's 64 lanes (all active): a Hillis-Steele scan
-// inside each row of 16 lanes by DPP row shifts (a lane with no source lane adds 0), then
-// each row adds the totals of the rows before it, read from lanes 15, 31 and 47.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
-  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-            r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = lane >> 4;
-  return v + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
-}
-
-__device__ __forceinline__ uint64_t peer_mask(int key, bool valid) {
-  uint64_t peers = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const bool bit = (key >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  return peers;
-}
 
 // FUSED: the kernel first runs top-k on `logits` for every token (one wavefront per token),
 // writing ids/w to global memory and the ids to LDS, and then sorts from LDS.
@@ -315,6 +290,10 @@ __global__ __launch_bounds__(256) void k_perm_scan(int nb, int E, int32_t* __res
   chunk_hist[(size_t)nb * E + e] = run;
 }
 
+// Up to 64 rows: the one-wavefront sort (with the top-k first when logits are given; 16
+// wavefronts select up to 16 tokens at once).  grid: 1; block 1024
+__global__ __launch_bounds__(1024) void k_permute_small(const SortArgs p) { small_topk_sort(p); }
+
 }  // namespace
 
 hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t* counts,
@@ -322,6 +301,11 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
                           int tile_m, hipStream_t s) {
   const int N = T * L.k;
   int32_t* idsm = const_cast<int32_t*>(ids);
+  if (N <= kSmallSortRows) {
+    const SortArgs p{T, L.k, L.E, L.S, tile_m, L.renorm, capacity_rows(L, T), nullptr, nullptr, idsm,
+                     counts, offsets, perm, inv_perm, plan};
+    return launch(MOE_KERNEL_PERMUTE, k_permute_small, 1, 1024, 0, s, p);
+  }
   if (N <= kSingleMaxRows)
     return launch(MOE_KERNEL_PERMUTE, k_permute<false>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m,
                   nullptr, 0, nullptr, idsm, counts, offsets, perm, inv_perm, plan, nullptr,
@@ -344,6 +328,11 @@ bool topk_permute_fusable(const LayerDims& L, int T) { return (size_t)T * L.k <=
 hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, int32_t* ids,
                                float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                                int32_t* inv_perm, int32_t* plan, int tile_m, hipStream_t s) {
+  if ((size_t)T * L.k <= kSmallSortRows) {
+    const SortArgs p{T, L.k, L.E, L.S, tile_m, L.renorm, capacity_rows(L, T), logits, topk_w, ids,
+                     counts, offsets, perm, inv_perm, plan};
+    return launch(MOE_KERNEL_PERMUTE, k_permute_small, 1, 1024, 0, s, p);
+  }
   return launch(MOE_KERNEL_PERMUTE, k_permute<true>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m, logits,
                 L.renorm, topk_w, ids, counts, offsets, perm, inv_perm, plan, nullptr,
                 capacity_rows(L, T));

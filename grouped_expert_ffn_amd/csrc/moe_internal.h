@@ -128,6 +128,7 @@ __device__ __forceinline__ float wave_max_u(float v) {
 constexpr int kPlanHeader = 4;
 constexpr int kMinTileM = 16;
 constexpr int kPermChunk = 1024;  // rows per workgroup of the multi-workgroup sort
+constexpr int kSmallSortRows = kWave;  // rows (T*k) the one-wavefront sort takes
 inline size_t plan_max_tiles(int T, int k, int E, int S) {
   const size_t N = (size_t)T * k;
   return N / kMinTileM + (size_t)E + (size_t)S * ((T + kMinTileM - 1) / kMinTileM) + 1;

@@ -110,17 +110,35 @@ def ids_case(kind, T, E, k, seed):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("T,E,k,S_", [(1, 8, 2, 0), (16, 8, 2, 0), (1, 64, 8, 0), (37, 64, 6, 2),
+# T*k up to 64 takes the one-wavefront sort (1-64 rows, up to 256 experts and 8 shared),
+# beyond the workgroup sort, past 4096 rows the chunked one
+@pytest.mark.parametrize("T,E,k,S_", [(1, 8, 2, 0), (16, 8, 2, 0), (1, 64, 8, 0), (8, 64, 8, 0),
+                                      (10, 64, 6, 2), (64, 8, 1, 0), (9, 256, 7, 8), (37, 64, 6, 2),
                                       (64, 64, 8, 0), (300, 256, 16, 1), (2048, 64, 8, 0),
                                       (2048, 64, 6, 2), (1000, 3, 1, 0), (513, 64, 8, 8),
                                       (2100, 64, 8, 0)])
 @pytest.mark.parametrize("kind", ["uniform", "same", "zipf"])
 def test_permute_is_bit_exact(T, E, k, S_, kind):
+    _permute_case(T, E, k, S_, kind, d=64)
+
+
+# layers whose FFN at these sizes is the GEMM, so the plan carries its M-tile list (d = 48 is
+# not a multiple of the matrix-core GEMV's 64): one-wavefront sort (40 and 64 rows) and
+# workgroup sort (65 rows)
+@pytest.mark.parametrize("T,E,k,S_", [(40, 8, 1, 1), (32, 4, 2, 2), (65, 8, 1, 0)])
+@pytest.mark.parametrize("kind", ["uniform", "zipf"])
+def test_permute_tile_list_is_bit_exact(T, E, k, S_, kind):
+    from grouped_expert_ffn_amd import abi, make_desc
+    assert abi.moe_ffn_kernel(make_desc(48, E, k, 48, n_shared=S_), T) == abi.MOE_FFN_GEMM
+    _permute_case(T, E, k, S_, kind, d=48)
+
+
+def _permute_case(T, E, k, S_, kind, d):
     from grouped_expert_ffn_amd import (MOE_WS_PERMUTE, alloc_workspace, make_desc, moe_permute,
                                         moe_workspace_bytes, to_device)
     t = T_()
     ids = ids_case(kind, T, E, k, seed=T + E + k)
-    desc = make_desc(64, E, k, 64, n_shared=S_)
+    desc = make_desc(d, E, k, d, n_shared=S_)
     dev = "cuda"
     counts = t.full((E,), -7, dtype=t.int32, device=dev)
     offsets = t.full((E + S_ + 1,), -7, dtype=t.int32, device=dev)
@@ -146,6 +164,8 @@ def test_permute_is_bit_exact(T, E, k, S_, kind):
         tiles = pl[4 + E + S_: 4 + E + S_ + 2 * pl[1]].reshape(-1, 2)
         expect = [(g, m0) for g in touched for m0 in range(0, c_ref[g] if g < E else T, tm)]
         assert [tuple(x) for x in tiles.tolist()] == expect
+    else:
+        assert d == 64
 
 
 # ----------------------------------------------------------------------------------------
@@ -282,9 +302,19 @@ def test_steps_every_row_deepseek_2048():
 
 
 # moe_forward against the five step-by-step calls, bit for bit, at decode and prefill sizes
-@pytest.mark.parametrize("wl,T", [(S.TINY_F32, 16), (SMALL_RAGGED, 100), (S.OLMOE_BF16, 8),
-                                  (S.OLMOE_BF16, 1), (S.DEEPSEEK_BF16, 4), (S.OLMOE_I8, 8),
-                                  (S.DEEPSEEK_BF16, 512), (S.OLMOE_I8, 64)], ids=case_id)
+# (the forward fuses the top-k into the sort; the steps sort given ids: up to 64 rows both
+# with the one-wavefront sort, from 65 rows with the workgroup sort)
+TINY_F32_SHARED = dataclasses.replace(S.TINY_F32, name="tiny_f32_shared", cid=83, S=1)
+FORWARD_CASES = [
+    (S.TINY_F32, 16), (SMALL_RAGGED, 100), (S.OLMOE_BF16, 8), (S.OLMOE_BF16, 1), (S.OLMOE_BF16, 2),
+    (S.OLMOE_BF16, 9), (S.DEEPSEEK_BF16, 4), (S.DEEPSEEK_BF16, 1), (S.DEEPSEEK_BF16, 7),
+    (S.DEEPSEEK_BF16, 8), (S.DEEPSEEK_I8, 3), (S.OLMOE_I8, 8), (S.OLMOE_I8, 1), (S.TINY_F32, 5),
+    (TINY_F32_SHARED, 8), (TINY_F32_SHARED, 9), (SMALL_RAGGED, 7), (SMALL_RAGGED_I8, 5),
+    (EDGE_MIN, 5), (EDGE_MAX, 4), (EDGE_MAX, 5), (SMALL_RING64, 8), (S.DEEPSEEK_BF16, 512),
+    (S.OLMOE_I8, 64)]
+
+
+@pytest.mark.parametrize("wl,T", FORWARD_CASES, ids=case_id)
 def test_forward_matches_steps_and_is_deterministic(wl, T):
     from grouped_expert_ffn_amd import to_device
     t = T_()
@@ -489,7 +519,8 @@ def test_permute_with_capacity_is_bit_exact(T, E, k, S_, cf):
 
 CAP_CASES = [(SMALL_ZIPF, 300, 1.0), (SMALL_RING, 300, 1.0), (SMALL_RING, 40, 0.5),
              (S.OLMOE_BF16, 8, 1.0), (S.OLMOE_I8_ZIPF, 8, 1.0), (S.DEEPSEEK_BF16, 2048, 1.0),
-             (S.DEEPSEEK_BF16, 16, 2.0), (SMALL_MFV, 32, 1.0)]
+             (S.DEEPSEEK_BF16, 16, 2.0), (SMALL_MFV, 32, 1.0), (S.DEEPSEEK_BF16, 6, 0.5),
+             (SMALL_ZIPF, 8, 0.5)]
 
 
 @pytest.mark.parametrize("wl,T,cf", CAP_CASES, ids=case_id)
@@ -521,7 +552,8 @@ def test_forward_with_capacity(wl, T, cf):
 # ----------------------------------------------------------------------------------------
 # the layer captured in a HIP graph: every replay equals the eager result bit for bit
 # ----------------------------------------------------------------------------------------
-@pytest.mark.parametrize("wl,T", [(S.OLMOE_BF16, 8), (SMALL_RING, 300), (S.DEEPSEEK_BF16, 16)],
+@pytest.mark.parametrize("wl,T", [(S.OLMOE_BF16, 8), (SMALL_RING, 300), (S.DEEPSEEK_BF16, 16),
+                                  (S.DEEPSEEK_BF16, 4)],
                          ids=case_id)
 def test_forward_graph_replay_matches_eager(wl, T):
     from grouped_expert_ffn_amd import abi, to_device
