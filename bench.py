@@ -21,8 +21,8 @@ events through the library's one-shot timing hook, for the roofline.  The same
 steps are also captured once in a HIP graph and replayed (checked bit for bit
 against the eager result first).
 
-After the headline, the other workload points are timed (``--sweep``), then the
-16-layer prefill stack (RMSNorm + MoE + residual per layer, T=2048, Zipf
+After the headline, the other workload points are timed (``--sweep``; each the
+median of three windows of at least 5 ms of steps), then the 16-layer prefill stack (RMSNorm + MoE + residual per layer, T=2048, Zipf
 routing with the busiest expert at about 4x the mean), then the oracle on the
 host cores as a reported CPU baseline.
 
@@ -150,7 +150,8 @@ def time_steps(step, steps, warmup):
 def warm_up(step, copies, min_s=0.05):
     """Untimed steps for the sweep and capacity points: two rotations over the weight copies,
     then more until at least `min_s` seconds of GPU work have run (the first passes over a
-    copy pay page-table walks, and the clocks take tens of ms to settle).  Returns the count."""
+    copy pay page-table walks, and the clocks take tens of ms to settle).  Returns the count
+    and the ms of one step measured on the way."""
     import torch
     n = 2 * copies
     for i in range(n):
@@ -166,7 +167,16 @@ def warm_up(step, copies, min_s=0.05):
     extra = max(0, int(min_s / per_step) - n)
     for i in range(extra):
         step(i)
-    return n + extra
+    return n + extra, per_step * 1e3
+
+
+def time_steps_median(step, steps, per_step_ms, windows=3, min_window_ms=5.0):
+    """The sweep and capacity points: the median of `windows` timed windows, each of at least
+    `steps` steps and `min_window_ms` of GPU work, so that one slow step in a short window
+    (a decode layer takes 30 µs) does not move the point."""
+    n = max(steps, int(min_window_ms / max(per_step_ms, 1e-3)) + 1)
+    runs = sorted(time_steps(step, n, 0) for _ in range(windows))
+    return runs[len(runs) // 2]
 
 
 def step_percentiles(step, n):
@@ -433,11 +443,12 @@ def measure(wl, T, steps, warmup, copies, extras=False):
     gate = oracle_gate(wl, pt.host, pt.x_host, pt.y_host, ids, gate_tokens(T), what=f"{wl.name} T={T}")
     n_touched = int(np.count_nonzero(np.bincount(ids.ravel(), minlength=wl.E)))
     work = layer_work(wl, T, n_touched)
-    if warmup is None:
-        warm_up(pt.step, copies)
-        warmup = 0
-    ms, wall = time_steps(pt.step, steps, warmup)
-    launches = max(10, min(steps, 50))
+    if warmup is None:  # a sweep point
+        _, per_step = warm_up(pt.step, copies)
+        ms, wall = time_steps_median(pt.step, steps, per_step)
+    else:
+        ms, wall = time_steps(pt.step, steps, warmup)
+    launches = 50  # the average over 50 launches, as rocprofv3's kernel statistics report it
     gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, pt.step, launches)
     dn_ms, _ = time_kernel(abi.MOE_KERNEL_DOWN, pt.step, launches)
     hbm, mfma = _fracs(work, ms)
@@ -596,8 +607,8 @@ def measure_capacity(wl, T, cf, steps, copies):
     ids = pt.sanity_gate()
     cap, dropped = drop_stats(ids, wl.E, cf)
     gate = capacity_gate(wl, pt, ids, cf, dropped)
-    warm_up(pt.step, copies)
-    ms, _ = time_steps(pt.step, steps, 0)
+    _, per_step = warm_up(pt.step, copies)
+    ms, _ = time_steps_median(pt.step, steps, per_step)
     pt.free()
     counts = np.bincount(ids.ravel(), minlength=wl.E)
     return {"workload": wl.name, "tokens": T, "capacity_factor": cf, "capacity_rows": cap,
