@@ -210,8 +210,9 @@ typedef enum {
  * `kernel` made by this thread (through any entry point) records start_event and stop_event
  * on that launch's stream, and the hook is then cleared.  A step that is one launch hands
  * the events to the launch itself (hipExtLaunchKernel), so they hold the kernel's own start
- * and end, the window a profiler's kernel trace reports; the multi-workgroup sort (two
- * launches) is bracketed by hipEventRecord before the first and after the second.  The events (hipEvent_t) are created and owned by the caller;
+ * and end, the window a profiler's kernel trace reports; the multi-workgroup sort (three
+ * launches: chunk histograms, their scan, the sort) is bracketed by hipEventRecord before the
+ * first and after the last.  The events (hipEvent_t) are created and owned by the caller;
  * NULL events disarm the hook.  Returns MOE_ERR_INVALID for an unknown kernel. */
 int32_t moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event);
 

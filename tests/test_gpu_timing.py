@@ -1,6 +1,6 @@
 """The per-kernel timing hook (moe_time_next_launch) that bench.py's roofline figures rest
 on: every kernel of a forward gets a positive time, the times fit inside the step, the hook
-fires once, and the two-launch sort (past one workgroup's rows) is bracketed as a whole."""
+fires once, and the multi-launch sort (past one workgroup's rows) is bracketed as a whole."""
 import pytest
 
 import moe_synth as S
@@ -68,9 +68,9 @@ def test_hook_fires_once():
     assert c.elapsed_time(d) > 0
 
 
-def test_two_launch_sort_is_bracketed():
-    # T*k past one workgroup's rows: the sort is a histogram launch plus the sort launch,
-    # and the hook brackets both
+def test_multi_launch_sort_is_bracketed():
+    # T*k past one workgroup's rows: the sort is a histogram launch, a scan and the sort launch,
+    # and the hook brackets all three
     from grouped_expert_ffn_amd import abi
     t = C.torch()
     gl, x = _layer(S.OLMOE_BF16, 600)  # 4800 rows
