@@ -410,6 +410,39 @@ def test_round_to_bf16_ties_and_pattern():
     assert np.all(m * 256 == np.rint(m * 256))
 
 
+def test_stack_layer_input_is_the_rounded_norm():
+    # [3, -4] at eps = 0 normalises to 3/sqrt(12.5) = 0.84853..., -1.13137...: neither is a
+    # bf16 value, and their nearest bf16 values are 0.84765625 (217/256) and -1.1328125 (-145/128)
+    y = O.stack_layer_input(np.array([[3.0, -4.0]]), 0.0)
+    assert y.tolist() == [[217 / 256, -145 / 128]]
+    # a constant row normalises to exactly +-1 at eps = 0, which bf16 holds
+    assert O.stack_layer_input(np.full((1, 8), -2.5), 0.0).tolist() == [[-1.0] * 8]
+    # every output has at most 8 significant bits and lies within half a bf16 ulp of the norm
+    h = np.random.default_rng(3).standard_normal((4, 64))
+    y = O.stack_layer_input(h, 1e-5)
+    m, _ = np.frexp(y)
+    assert np.all(m * 256 == np.rint(m * 256))
+    ref = h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + 1e-5)
+    assert np.all(np.abs(y - ref) <= np.abs(ref) * 2.0 ** -8 * (1 + 1e-12))
+
+
+def test_full_route_is_router_then_topk():
+    # unit router rows pick columns (2, 0, 3, 1) of x, a bias adds (0, 0, 10, 0): the logits are
+    # x[:, [2, 0, 3, 1]] + bias, and the top-2 is chosen from them
+    x = np.array([[0.5, 1.5, -1.0, 2.0, 9.0],
+                  [3.0, 0.0, 1.0, 0.25, -9.0]])
+    w_r = np.zeros((4, 5))
+    for e, c in enumerate((2, 0, 3, 1)):
+        w_r[e, c] = 1.0
+    bias = np.array([0.0, 0.0, 10.0, 0.0])
+    logits, ids, w = O.full_route(x, w_r, bias, 2, True)
+    np.testing.assert_array_equal(logits, [[-1.0, 0.5, 12.0, 1.5], [1.0, 3.0, 10.25, 0.0]])
+    assert ids.tolist() == [[2, 3], [2, 1]]
+    # renormalised over the two chosen: e^l / (e^l + e^l')
+    np.testing.assert_allclose(w[0], [1 / (1 + math.exp(1.5 - 12.0)), 1 / (1 + math.exp(12.0 - 1.5))], rtol=1e-14)
+    np.testing.assert_allclose(w[1], [1 / (1 + math.exp(3.0 - 10.25)), 1 / (1 + math.exp(10.25 - 3.0))], rtol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # option: capacity-factor dropping
 # --------------------------------------------------------------------------
