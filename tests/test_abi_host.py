@@ -211,3 +211,26 @@ def test_noalloc_refuses_a_layer_beyond_its_scratch_and_takes_zero_tokens(L):
     with pytest.raises(abi.MoeError) as ei:
         abi.moe_forward_noalloc(d, 4, None, 0x1000, None, w, None, 0x1000, None, None, stream=0)
     assert ei.value.status == abi.MOE_ERR_INVALID
+
+
+def test_last_error_is_per_thread(L):
+    # each thread sees the message of its own last refusal, whatever the other threads did
+    import ctypes
+    import threading
+    results = {}
+    barrier = threading.Barrier(2)
+
+    def refuse(name, T, top_k):
+        d = desc(top_k=top_k)
+        barrier.wait(timeout=30)
+        for _ in range(200):
+            st = L.moe_ffn_kernel(ctypes.byref(d), T)
+            msg = L.moe_last_error().decode()
+        results[name] = (st, msg)
+
+    a = threading.Thread(target=refuse, args=("tokens", 0, 8))
+    b = threading.Thread(target=refuse, args=("top_k", 8, 65))
+    a.start(); b.start(); a.join(timeout=60); b.join(timeout=60)
+    assert results["tokens"][0] == abi.MOE_ERR_INVALID and "T = 0" in results["tokens"][1]
+    assert results["top_k"][0] < 0 and "T = 0" not in results["top_k"][1]
+    assert "top_k" in results["top_k"][1] or "k =" in results["top_k"][1], results["top_k"][1]
