@@ -726,23 +726,6 @@ __global__ __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-// Raise a kernel's dynamic-LDS limit once per device (the attribute belongs to the current
-// device; the flags are indexed by device ordinal and safe to race on).
-constexpr int kMaxDevices = 64;
-typedef std::atomic<bool> LdsFlags[kMaxDevices];
-template <typename F>
-hipError_t set_lds(F* kernel, size_t bytes, LdsFlags& done) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
-  return e;
-}
-
 // The ring kernel serves bf16 and int8 weights when both K dimensions are multiples of its
 // K-step; both launches of a layer must use the same M-tile (it is baked into the launch plan).
 bool use_ring(const LayerDims& L) {

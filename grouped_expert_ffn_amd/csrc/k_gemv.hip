@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
       for (int t = 0; t < NMAT; ++t)
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-          const float v = sum8(acc[c][t][m]);
+          const float v = sum8(settle_dot(acc[c][t][m]));
           if (m == q) red[wave][c][t][m][lg] = v;
         }
     __syncthreads();
@@ -505,19 +505,266 @@ hipError_t dispatch_gemv_mfma(const GemvArgs& a, int slots, hipStream_t s) {
   if (nbk <= 24) return run_gemv_mfma<MODE, W8, 2, 6>(a, slots, s);
   return run_gemv_mfma<MODE, W8, 2, 8>(a, slots, s);
 }
+
+
+// ---------------------------------------------------------------------------------------
+// Down projection and combine in one launch, for decode sizes inside moe_forward.
+//
+// The combine needs every row routed to an output channel, so a block here owns 8 output
+// channels across all of the launch's touched groups (where k_gemv's block owns them for one
+// group): it walks the group list, streams each group's 8 weight rows (one contiguous 8 x K
+// stretch), keeps the rows' partial sums in LDS and, at the end, sums each token's rows for
+// its channels and writes y.  No block waits for another and the rows never leave LDS, which
+// saves the combine's launch and its round trip through memory.
+//
+//  * Lane layout and arithmetic are k_gemv's (MODE 1): K split over the four wavefronts in
+//    spw 8-lane steps each, eight lanes per channel, the same dot-product order, the DPP sum
+//    over the 8 lanes, the fixed-order sum over wavefronts, the int8 scale and the rounding
+//    to the activation type; the sum over a token's rows then follows k_combine's order with
+//    its single rounding.  y is therefore bit-identical to the two launches.
+//  * Each wavefront first stages its own K-slice of all R activation rows into a private LDS
+//    region by direct-to-LDS loads, so no barrier is needed before the end; it waits for all
+//    its loads once, behind the first D groups' weights, before the first sum.
+//  * The weights stream through registers in a ring of D groups: while one group's rows are
+//    summed, the next D-1 groups' loads are in flight.  Every weight load is unconditional
+//    (a lane past its columns reads an in-bounds piece and skips the math), so the number of
+//    loads in flight is a compile-time constant and the compiler's waits leave the ring
+//    running; the ring's tail re-reads the last group D times (a cache hit).
+// grid: ceil(N / 8); block 256; one pass covers K (MAXIT == spw); dynamic LDS from
+// down_combine_geom().
+struct DownCombineArgs {
+  const void* h;            // [R, K] gate/up output by sorted row
+  const void* w;            // [G, N, K] down weights
+  const float* s;           // int8 per-channel scales [G, N], else null
+  const int32_t* offsets;
+  const int32_t* plan;
+  const int32_t* inv_perm;  // [T * k], -1 for a dropped slot
+  const float* topk_w;      // [T * k]
+  const void* residual;     // [T, N] or null
+  void* y;                  // [T, N]
+  int T, k, S, E, K, N;
+  int R;                    // rows: T * k + S * T
+  int slice;                // LDS bytes of one row's wavefront slice: spw * 8 * V * sizeof(AT)
+};
+
+constexpr int kDcRing = 2;  // groups in each stream's weight ring (deeper rings measured slower)
+// Slot streams per workgroup (four wavefronts each): more streams keep more groups' weights in
+// flight per CU.  Measured against one, two and four: two for bf16 weights (OLMoE T=8 layer
+// 108-110 against 109-111 us with four), four for int8, whose groups carry half the bytes for
+// the same fixed cost per group (T=8 65 against 68 us).
+template <typename WT>
+constexpr int dc_streams() { return sizeof(WT) == 1 ? 4 : 2; }
+constexpr size_t kDcMaxLds = 160 * 1024;  // one workgroup per CU
+
+template <typename AT, typename WT, int MAXIT, int MB, int NG>
+__global__ __launch_bounds__(256 * NG) void k_down_combine(const DownCombineArgs a) {
+  constexpr int V = WTraits<WT>::V;
+  constexpr int STEP = 8 * V;
+  constexpr bool I8 = sizeof(WT) == 1;
+  constexpr int D = kDcRing;
+  typedef Dot<AT, WT> Dt;
+  extern __shared__ __align__(16) unsigned char lds[];
+
+  const int R = a.R, K = a.K, N = a.N, T = a.T, k = a.k, Tk = T * k;
+  const int tid = threadIdx.x;
+  // the wavefront index made visibly uniform: the group lookups below stay scalar loads, and
+  // the ring's loop stays a uniform loop (as a divergent one, every lookup became a vector
+  // load whose wait drained the ring)
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int kw = wave % kWaves, grp = wave / kWaves;  // K-slice, and the slot stream
+  const int q = lane % 8, lg = lane / 8;
+  const int n0 = blockIdx.x * 8;
+  const int n = min(n0 + lg, N - 1);  // this lane's channel (clamped: results past N unused)
+  unsigned char* xw = lds + (size_t)kw * R * a.slice;                             // [R][slice]
+  float* part = reinterpret_cast<float*>(lds + (size_t)kWaves * R * a.slice);     // [4][R][8]
+  float* scl = part + (size_t)kWaves * R * 8;                                     // [R][8]
+  int32_t* c_row = reinterpret_cast<int32_t*>(scl + (I8 ? (size_t)R * 8 : 0));   // [T * k]
+  float* c_w = reinterpret_cast<float*>(c_row + Tk);                             // [T * k]
+
+  // (0) the combine's inputs, loaded now and used at the end: one routed slot per thread,
+  //     and the residual of thread (token tid / 8, channel tid % 8)
+  int my_row = -1;
+  float my_w = 0.f;
+  if (tid < Tk) {
+    my_row = a.inv_perm[tid];
+    my_w = a.topk_w[tid];
+  }
+  const int ct = tid / 8, cn = n0 + tid % 8;
+  // raw and unconditional (a thread past the tokens, or no residual, reads an in-bounds
+  // element it ignores), so the load is only waited for where the value is used, at the end
+  const AT* rsrc = a.residual ? reinterpret_cast<const AT*>(a.residual) + (size_t)min(ct, T - 1) * N + min(cn, N - 1)
+                              : reinterpret_cast<const AT*>(a.h);
+  const AT resid = *rsrc;
+
+  // (1) K-slice kw of every row into its LDS region, shared by the NG wavefronts of that
+  //     slice (64 pieces each in turn): piece c of the region is row c / cpr, 16 bytes at
+  //     column kw0 + (c % cpr) * 16 / sizeof(AT)
+  const int steps = (K + STEP - 1) / STEP;
+  const int spw = a.slice / (STEP * (int)sizeof(AT));
+  const int s_lo = kw * spw, s_hi = min(steps, s_lo + spw);
+  const int kw0 = s_lo * STEP;
+  const AT* h = reinterpret_cast<const AT*>(a.h);
+  if (s_lo < steps) {
+    const int cpr = a.slice / 16;
+    const int dr = NG * kWave / cpr, dp = NG * kWave % cpr;  // (row, piece) advance per turn
+    int r = (grp * kWave + lane) / cpr, p = (grp * kWave + lane) % cpr;
+    for (int c0 = grp * kWave; c0 < R * cpr; c0 += NG * kWave) {
+      int col = kw0 + p * (16 / (int)sizeof(AT));
+      if (col >= K) col = kw0;  // the last wavefront's slice past K: an in-bounds piece, never read
+      if (r < R)
+        __builtin_amdgcn_global_load_lds((gmem_void*)(h + (size_t)r * K + col), (lds_void*)(xw + c0 * 16),
+                                         16, 0, 0);
+      r += dr;
+      p += dp;
+      if (p >= cpr) {
+        p -= cpr;
+        ++r;
+      }
+    }
+  }
+
+  // (2) the weight ring over the touched groups: slot stream grp takes groups grp, grp + NG, ...
+  const cint32* plan = (const cint32*)a.plan;
+  const cint32* offs = (const cint32*)a.offsets;
+  const WT* wbase = reinterpret_cast<const WT*>(a.w);
+  const int nslots = plan[0], cap = plan[3];
+  const int mine = nslots > grp ? (nslots - grp + NG - 1) / NG : 0;  // this stream's groups
+  uint4 wb[D][MAXIT];
+  float sc[D];
+  auto issue = [&](int i, int j) {
+    const int g = plan[kPlanHeader + grp + i * NG];
+    const WT* wp = wbase + ((size_t)g * N + n) * K;
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int col = kw0 + it * STEP + q * V;
+      const int colc = (s_lo + it < s_hi && col < K) ? col : (q * V < K ? q * V : 0);
+      wb[j][it] = *reinterpret_cast<const uint4*>(wp + colc);
+    }
+    if (I8) sc[j] = a.s[(size_t)g * N + n];
+  };
+  auto process = [&](int i, int j) {
+    const int g = plan[kPlanHeader + grp + i * NG];
+    const int r0 = offs[g];
+    const int Mg = offs[g + 1] - r0;
+    const int M = (g < a.E && cap > 0) ? min(Mg, cap) : Mg;  // capacity: the rest is dropped
+    for (int m0 = 0; m0 < M; m0 += MB) {
+      float acc[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) acc[m] = 0.f;
+#pragma unroll
+      for (int it = 0; it < MAXIT; ++it) {
+        const int xcol = it * STEP + q * V;  // column within the slice
+        if (s_lo + it < s_hi && kw0 + xcol < K) {
+          const typename Dt::W wv = Dt::prep(wb[j][it]);
+          const unsigned char* xp = xw + (size_t)(r0 + m0) * a.slice + xcol * (int)sizeof(AT);
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+            if (m0 + m < M) acc[m] = Dt::run(wv, xp + m * a.slice, acc[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const float v = sum8(settle_dot(acc[m]));
+        if (m0 + m < M && q == (m & 7)) {
+          const int r = r0 + m0 + m;
+          part[((size_t)kw * R + r) * 8 + lg] = v;
+          if (I8 && kw == 0) scl[(size_t)r * 8 + lg] = sc[j];
+        }
+      }
+    }
+  };
+  if (mine > 0) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue(min(j, mine - 1), j);
+  }
+  // the staged rows are in and visible to every wavefront (this also waits for the first
+  // groups' weights, which their sums needed anyway; direct-to-LDS loads are not ordered with
+  // the register loads behind them, so no partial wait would do)
+  __syncthreads();
+  if (mine > 0) {
+    for (int i0 = 0; i0 < mine; i0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (i0 + j < mine) process(i0 + j, j);
+        issue(min(i0 + j + D, mine - 1), j);
+      }
+    }
+  }
+
+  // (3) every wavefront's partial sums are in: each thread (token, channel) sums the token's
+  //     rows in the combine's order
+  if (tid < Tk) {
+    c_row[tid] = my_row;
+    c_w[tid] = my_w;
+  }
+  __syncthreads();
+  if (ct < T && cn < N) {
+    const int c = tid % 8;
+    auto row = [&](int r) {
+      float v = (part[(size_t)r * 8 + c] + part[((size_t)R + r) * 8 + c]) +
+                (part[((size_t)2 * R + r) * 8 + c] + part[((size_t)3 * R + r) * 8 + c]);
+      if (I8) v *= scl[(size_t)r * 8 + c];
+      return Act<AT>::round(v);
+    };
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int r = c_row[ct * k + j];
+      if (r >= 0) acc = fmaf(c_w[ct * k + j], row(r), acc);
+    }
+    for (int sx = 0; sx < a.S; ++sx) acc = acc + row(Tk + sx * T + ct);
+    if (a.residual) acc = acc + Act<AT>::load(&resid, 0);
+    Act<AT>::store(reinterpret_cast<AT*>(a.y), (size_t)ct * N + cn, acc);
+  }
+}
+
+template <typename AT, typename WT, int MB>
+hipError_t run_down_combine(const DownCombineArgs& a, int spw, size_t lds, hipStream_t s) {
+  constexpr int NG = dc_streams<WT>();
+  switch (spw) {
+#define DC_CASE(MAXIT)                                                                             \
+  case MAXIT: {                                                                                     \
+    static LdsFlags done;                                                                           \
+    hipError_t e = set_lds(&k_down_combine<AT, WT, MAXIT, MB, NG>, kDcMaxLds, done);               \
+    if (e != hipSuccess) return e;                                                                  \
+    /* the combine's hook brackets the launch it shares with the down projection */                \
+    LaunchTimer combine_timer(MOE_KERNEL_COMBINE, s);                                              \
+    return launch(MOE_KERNEL_DOWN, k_down_combine<AT, WT, MAXIT, MB, NG>, dim3((a.N + 7) / 8), 256 * NG, \
+                  lds, s, a);                                                                       \
+  }
+    DC_CASE(1)
+    DC_CASE(2)
+    DC_CASE(3)
+    DC_CASE(4)
+    DC_CASE(5)
+    DC_CASE(6)
+    DC_CASE(7)
+    DC_CASE(8)
+#undef DC_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename AT, typename WT>
+hipError_t dispatch_down_combine(const DownCombineArgs& a, int spw, size_t lds, hipStream_t s) {
+  return a.T == 1 ? run_down_combine<AT, WT, 1>(a, spw, lds, s) : run_down_combine<AT, WT, 4>(a, spw, lds, s);
+}
 }  // namespace
 
-hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
-  const int slots = (T * L.k < L.E ? T * L.k : L.E) + L.S;
+namespace {
+GemvArgs gemv_args(const LayerDims& L, const FfnArgs& f) {
   GemvArgs a{};
   a.offsets = f.offsets;
   a.perm = f.perm;
   a.plan = f.plan;
   a.k = L.k;
   a.E = L.E;
-  hipError_t err;
+  return a;
+}
 
-  // gate/up + SwiGLU
+// gate/up + SwiGLU on the VALU GEMV
+hipError_t gemv_gate_up(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
+  const int slots = (T * L.k < L.E ? T * L.k : L.E) + L.S;
+  GemvArgs a = gemv_args(L, f);
   a.in = f.x;
   a.w0 = f.w_gate;
   a.w1 = f.w_up;
@@ -526,15 +773,43 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.h;
   a.K = L.d;
   a.N = L.I;
-  if (L.act == MOE_F32)
-    err = dispatch_gemv<0, float, float>(a, T, slots, s);
-  else if (L.wdt == MOE_I8)
-    err = dispatch_gemv<0, uint16_t, int8_t>(a, T, slots, s);
-  else
-    err = dispatch_gemv<0, uint16_t, uint16_t>(a, T, slots, s);
-  if (err != hipSuccess) return err;
+  if (L.act == MOE_F32) return dispatch_gemv<0, float, float>(a, T, slots, s);
+  if (L.wdt == MOE_I8) return dispatch_gemv<0, uint16_t, int8_t>(a, T, slots, s);
+  return dispatch_gemv<0, uint16_t, uint16_t>(a, T, slots, s);
+}
 
-  // down
+// The fused launch's geometry: K steps per wavefront, a row's wavefront slice in LDS, the
+// rows, and the LDS it takes (staged rows, partial sums, int8 scales, the combine's slots).
+struct DownCombineGeom {
+  int spw, slice, R;
+  size_t lds;
+};
+DownCombineGeom down_combine_geom(const LayerDims& L, int T) {
+  const bool f32 = L.act == MOE_F32, i8 = L.wdt == MOE_I8;
+  const int V = f32 ? 4 : (i8 ? 16 : 8), esz = f32 ? 4 : 2;
+  const int steps = (L.I + 8 * V - 1) / (8 * V);
+  DownCombineGeom g;
+  g.spw = (steps + kWaves - 1) / kWaves;
+  g.slice = g.spw * 8 * V * esz;
+  g.R = T * L.k + L.S * T;
+  g.lds = (size_t)kWaves * g.R * g.slice + (size_t)kWaves * g.R * 8 * 4 + (i8 ? (size_t)g.R * 8 * 4 : 0) +
+          (size_t)T * L.k * 8;
+  return g;
+}
+}  // namespace
+
+bool gemv_down_combine_fits(const LayerDims& L, int T) {
+  const DownCombineGeom g = down_combine_geom(L, T);
+  // (int8 past 6 steps per wavefront would spill registers at four slot streams)
+  const int max_spw = L.wdt == MOE_I8 ? 6 : 8;
+  return T >= 1 && T * 8 <= 256 && T * L.k <= 256 && g.spw <= max_spw && g.lds <= kDcMaxLds;
+}
+
+hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {
+  hipError_t err = gemv_gate_up(L, T, f, s);
+  if (err != hipSuccess) return err;
+  const int slots = (T * L.k < L.E ? T * L.k : L.E) + L.S;
+  GemvArgs a = gemv_args(L, f);
   a.in = f.h;
   a.w0 = f.w_down;
   a.w1 = nullptr;
@@ -543,13 +818,22 @@ hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStrea
   a.out = f.rows;
   a.K = L.I;
   a.N = L.d;
-  if (L.act == MOE_F32)
-    err = dispatch_gemv<1, float, float>(a, T, slots, s);
-  else if (L.wdt == MOE_I8)
-    err = dispatch_gemv<1, uint16_t, int8_t>(a, T, slots, s);
-  else
-    err = dispatch_gemv<1, uint16_t, uint16_t>(a, T, slots, s);
-  return err;
+  if (L.act == MOE_F32) return dispatch_gemv<1, float, float>(a, T, slots, s);
+  if (L.wdt == MOE_I8) return dispatch_gemv<1, uint16_t, int8_t>(a, T, slots, s);
+  return dispatch_gemv<1, uint16_t, uint16_t>(a, T, slots, s);
+}
+
+hipError_t launch_gemv_ffn_combine(const LayerDims& L, int T, const FfnArgs& f, const int32_t* inv_perm,
+                                   const float* topk_w, const void* residual, void* y, hipStream_t s) {
+  if (!gemv_down_combine_fits(L, T)) return hipErrorInvalidValue;
+  hipError_t err = gemv_gate_up(L, T, f, s);
+  if (err != hipSuccess) return err;
+  const DownCombineGeom g = down_combine_geom(L, T);
+  DownCombineArgs a{f.h, f.w_down, f.s_down, f.offsets, f.plan, inv_perm, topk_w, residual, y,
+                    T, L.k, L.S, L.E, L.I, L.d, g.R, g.slice};
+  if (L.act == MOE_F32) return dispatch_down_combine<float, float>(a, g.spw, g.lds, s);
+  if (L.wdt == MOE_I8) return dispatch_down_combine<uint16_t, int8_t>(a, g.spw, g.lds, s);
+  return dispatch_down_combine<uint16_t, uint16_t>(a, g.spw, g.lds, s);
 }
 
 hipError_t launch_gemv_mfma_ffn(const LayerDims& L, int T, const FfnArgs& f, hipStream_t s) {

@@ -512,9 +512,15 @@ int32_t forward_impl(const moe_layer_desc_t* desc, int32_t T, const void* x, con
   FfnArgs a{xin, weights->w_gate, weights->w_up, weights->w_down, weights->s_gate, weights->s_up,
             weights->s_down, offsets, perm, plan, base + f.h, base + f.rows};
   if (L.wdt != MOE_I8) a.s_gate = a.s_up = a.s_down = nullptr;
-  if ((e = launch_grouped_ffn(L, T, a, s)) != hipSuccess) return device_fail(e, "grouped FFN launch");
-  if ((e = launch_combine(L, T, base + f.rows, inv_perm, w, residual, y, s)) != hipSuccess)
-    return device_fail(e, "combine launch");
+  if (ffn_path(L, T) == FfnPath::kGemv && gemv_down_combine_fits(L, T)) {
+    // decode sizes: the down projection and the combine in one launch
+    if ((e = launch_gemv_ffn_combine(L, T, a, inv_perm, w, residual, y, s)) != hipSuccess)
+      return device_fail(e, "grouped FFN + combine launch");
+  } else {
+    if ((e = launch_grouped_ffn(L, T, a, s)) != hipSuccess) return device_fail(e, "grouped FFN launch");
+    if ((e = launch_combine(L, T, base + f.rows, inv_perm, w, residual, y, s)) != hipSuccess)
+      return device_fail(e, "combine launch");
+  }
   if (topk_ids_out &&
       (e = hipMemcpyAsync(topk_ids_out, ids, (size_t)T * L.k * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
     return device_fail(e, "topk_ids copy");

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "moe.h"
@@ -65,10 +66,12 @@ template <typename AT> struct Act;
 template <> struct Act<float> {
   __device__ static float load(const float* p, size_t i) { return p[i]; }
   __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+  __device__ static float round(float v) { return v; }  // the value a store then load gives
 };
 template <> struct Act<uint16_t> {
   __device__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
   __device__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  __device__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
 // -------------------------------------------------------------------------------------
@@ -84,6 +87,15 @@ __device__ __forceinline__ float dpp(float v) {
 }
 // Sum over each aligned group of 8 lanes; every lane of the group gets the same bits
 // (each step adds a value and its partner, and fp addition is commutative).
+// A dot-product sum about to be read by DPP lane moves.  On gfx950 a DPP read two
+// instructions after v_dot2c_f32_bf16 wrote its source register has returned the value from
+// before that write (a row sum came out missing its last term), and the compiler may space the
+// two by only two instructions.  The asm ties the value, so nothing is scheduled across it, and
+// adds three wait states.
+__device__ __forceinline__ float settle_dot(float v) {
+  asm volatile("s_nop 2" : "+v"(v));
+  return v;
+}
 __device__ __forceinline__ float sum8(float v) {
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
@@ -161,6 +173,23 @@ hipError_t launch(int kernel, F f, dim3 grid, dim3 block, size_t lds, hipStream_
   return hipGetLastError();
 }
 
+// Raise a kernel's dynamic-LDS limit once per device (the attribute belongs to the current
+// device; the flags are indexed by device ordinal and safe to race on).
+constexpr int kMaxDevices = 64;
+typedef std::atomic<bool> LdsFlags[kMaxDevices];
+template <typename F>
+hipError_t set_lds(F* kernel, size_t bytes, LdsFlags& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
+  return e;
+}
+
 class LaunchTimer {
  public:
   LaunchTimer(int kernel, hipStream_t s);
@@ -221,6 +250,12 @@ hipError_t launch_grouped_ffn(const LayerDims& L, int T, const FfnArgs& a, hipSt
 // the matrix-core GEMV (bf16 activations, d and I multiples of 64), the MFMA GEMM
 hipError_t launch_gemv_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
 hipError_t launch_gemv_mfma_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
+// moe_forward at decode sizes: the VALU GEMV's gate/up, then the down projection and the
+// combine as one launch (y bit-identical to launch_gemv_ffn + launch_combine).  Applies when
+// the layer is on the VALU GEMV path and gemv_down_combine_fits(L, T).
+bool gemv_down_combine_fits(const LayerDims& L, int T);
+hipError_t launch_gemv_ffn_combine(const LayerDims& L, int T, const FfnArgs& a, const int32_t* inv_perm,
+                                   const float* topk_w, const void* residual, void* y, hipStream_t s);
 hipError_t launch_gemm_ffn(const LayerDims& L, int T, const FfnArgs& a, hipStream_t s);
 int gemm_tile_m(const LayerDims& L);
 

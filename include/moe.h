@@ -172,7 +172,11 @@ int32_t moe_combine(const moe_layer_desc_t* desc, int32_t T, const void* rows,
  * The normalised input is rounded to act_dtype and fed to both router and experts.
  * x [T,d]; residual [T,d] or NULL (may alias x or y); y [T,d] (may alias x).
  * topk_ids_out [T,k] / topk_w_out [T,k]: optional copies of the routing (NULL to skip).
- * ws >= moe_workspace_bytes(desc, T, MOE_WS_FORWARD). */
+ * ws >= moe_workspace_bytes(desc, T, MOE_WS_FORWARD).
+ * At decode sizes on the MOE_FFN_GEMV family, when every row's activations fit in one
+ * workgroup's LDS (up to 9 tokens on an OLMoE-shaped layer, 6 on a DeepSeek-MoE-shaped one),
+ * the down projection and the combine run as one launch; y is bit-identical to the separate
+ * steps either way. */
 int32_t moe_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, const void* w_router,
                     const float* router_bias, const moe_expert_weights_t* weights,
                     const void* residual, void* y, int32_t* topk_ids_out, float* topk_w_out,
@@ -212,7 +216,9 @@ typedef enum {
  * the events to the launch itself (hipExtLaunchKernel), so they hold the kernel's own start
  * and end, the window a profiler's kernel trace reports; the multi-workgroup sort (three
  * launches: chunk histograms, their scan, the sort) is bracketed by hipEventRecord before the
- * first and after the last.  The events (hipEvent_t) are created and owned by the caller;
+ * first and after the last.  Where moe_forward runs the down projection and the combine as
+ * one launch, MOE_KERNEL_DOWN holds that launch's own window and MOE_KERNEL_COMBINE brackets
+ * the same launch.  The events (hipEvent_t) are created and owned by the caller;
  * NULL events disarm the hook.  Returns MOE_ERR_INVALID for an unknown kernel. */
 int32_t moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event);
 

@@ -113,13 +113,14 @@ def sample_rows(offsets: np.ndarray, n_groups: int, R: int, n_random: int, seed:
     return sorted(rows)
 
 
-def run_steps(gl: GpuLayer, x_dev, T: int, logits_in=None):
-    """Route, permute, grouped FFN and combine through the separate C-ABI calls."""
+def run_steps(gl: GpuLayer, x_dev, T: int, logits_in=None, desc=None, residual=None):
+    """Route, permute, grouped FFN and combine through the separate C-ABI calls (with the
+    layer's own descriptor unless `desc` is given, and `residual` added in the combine)."""
     import torch as t
     from grouped_expert_ffn_amd import (MOE_WS_GROUPED_FFN, MOE_WS_PERMUTE, alloc_workspace,
                                         moe_combine, moe_grouped_ffn, moe_permute, moe_route,
                                         moe_workspace_bytes)
-    wl, d = gl.wl, gl.desc
+    wl, d = gl.wl, (desc if desc is not None else gl.desc)
     dev = x_dev.device
     k, E, S_ = wl.k, wl.E, wl.S
     R = T * k + S_ * T
@@ -143,7 +144,7 @@ def run_steps(gl: GpuLayer, x_dev, T: int, logits_in=None):
     moe_grouped_ffn(d, T, x_dev, gl.dev.weights, out["offsets"], out["perm"], out["plan"], out["rows"],
                     ws, wb)
     out["y"] = t.empty((T, wl.d), dtype=adt, device=dev)
-    moe_combine(d, T, out["rows"], out["inv_perm"], out["w"], None, out["y"])
+    moe_combine(d, T, out["rows"], out["inv_perm"], out["w"], residual, out["y"])
     t.cuda.synchronize()
     return out
 

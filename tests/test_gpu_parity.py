@@ -333,6 +333,35 @@ def test_forward_matches_steps_and_is_deterministic(wl, T):
     assert t.equal(y1, steps["y"])
 
 
+# moe_forward with a residual and a capacity limit against the separate calls, bit for bit.
+# At decode sizes (OLMoE shapes through T=9, DeepSeek shapes through T=6) the forward sums a
+# token's rows inside the down projection's launch; T=64 and T=7 take the two launches.
+RESID_CASES = [(S.OLMOE_BF16, 1, 0.0), (S.OLMOE_BF16, 8, 1.0), (S.OLMOE_BF16, 9, 0.0),
+               (S.DEEPSEEK_BF16, 5, 0.0), (S.DEEPSEEK_BF16, 6, 0.5), (S.DEEPSEEK_I8, 3, 0.5),
+               (S.OLMOE_I8, 2, 0.0), (TINY_F32_SHARED, 9, 0.0), (S.TINY_F32, 3, 1.0),
+               (SMALL_RAGGED_I8, 5, 0.5), (EDGE_MAX, 5, 0.0), (S.DEEPSEEK_BF16, 7, 0.0),
+               (S.OLMOE_BF16, 64, 0.0)]
+
+
+@pytest.mark.parametrize("wl,T,cf", RESID_CASES, ids=case_id)
+def test_forward_with_residual_and_capacity_matches_steps(wl, T, cf):
+    from grouped_expert_ffn_amd import DTYPES, DeviceLayer, make_desc, to_device
+    t = T_()
+    gl = C.GpuLayer(wl)
+    desc = make_desc(wl.d, wl.E, wl.k, wl.I, wl.S, wl.renormalize, DTYPES[wl.act], DTYPES[wl.wdt],
+                     capacity_factor=cf)
+    dl = DeviceLayer(desc, gl.dev.w_router, gl.dev.bias, gl.dev.w_gate, gl.dev.w_up, gl.dev.w_down,
+                     gl.dev.s_gate, gl.dev.s_up, gl.dev.s_down)
+    xd = to_device(S.make_tokens(wl, T))
+    res = to_device(S.make_tokens(wl, T, seed=11))
+    y = dl.forward(xd, residual=res)
+    steps = C.run_steps(gl, xd, T, desc=desc, residual=res)
+    t.cuda.synchronize()
+    if cf and cf <= 0.5:
+        assert (steps["inv_perm"] < 0).any(), "the case is meant to drop rows"
+    assert t.equal(y, steps["y"])
+
+
 @pytest.mark.parametrize("T", [4, 16])  # the decode GEMV and the prefill GEMM
 def test_forward_residual_and_power_of_two_scaling(T):
     from grouped_expert_ffn_amd import DeviceLayer, to_device

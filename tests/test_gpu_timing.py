@@ -24,10 +24,12 @@ def _layer(wl, T):
     return gl, to_device(S.make_tokens(wl, T))
 
 
-def test_every_kernel_of_a_forward_is_timed_inside_the_step():
+# T=8: the down projection and the combine run as one launch (decode sizes); T=64: separate
+@pytest.mark.parametrize("T,fused", [(8, True), (64, False)])
+def test_every_kernel_of_a_forward_is_timed_inside_the_step(T, fused):
     from grouped_expert_ffn_amd import abi
     t = C.torch()
-    wl, T = S.OLMOE_BF16, 8
+    wl = S.OLMOE_BF16
     gl, x = _layer(wl, T)
     gl.dev.forward(x)
     t.cuda.synchronize()
@@ -45,7 +47,12 @@ def test_every_kernel_of_a_forward_is_timed_inside_the_step():
     total = step[0].elapsed_time(step[1])
     print("kernel ms", [round(m, 4) for m in ms], "step ms", round(total, 4))
     assert all(m > 0 for m in ms), ms
-    assert sum(ms) <= total * 1.001, (ms, total)
+    if fused:
+        # the combine's hook brackets the launch whose own window the down projection's holds
+        assert ms[4] >= ms[3] * 0.999, ms
+        assert sum(ms[:4]) <= total * 1.001, (ms, total)
+    else:
+        assert sum(ms) <= total * 1.001, (ms, total)
     # the weight-streaming GEMVs dominate the decode layer
     assert ms[2] > ms[0] and ms[2] > ms[1] and ms[2] > ms[4]
 

@@ -407,3 +407,186 @@ def test_gemv_emulation_catches_a_wrong_row_rule():
     offsets, perm, cap, _ = routed_plan(wl, T, 0.0)
     with pytest.raises(AssertionError):
         check_gemv(wl, T, 0, offsets, np.arange(len(perm)) * wl.k * 2, cap)
+
+
+# ------------------------------------------------------------------------------------------
+# k_down_combine: the down projection and the combine in one launch (moe_forward, decode)
+# ------------------------------------------------------------------------------------------
+DC_MAX_LDS = 160 * 1024
+DC_RING = 2
+DC_STREAMS = {"i8": 4}  # slot streams per workgroup by weight type (else 2)
+
+
+def down_combine_geom(wl, T):
+    """(spw, slice, R, lds bytes) of the fused launch, as the launcher computes them."""
+    f32, i8 = wl.act == "f32", wl.wdt == "i8"
+    V, asz = (4, 4) if f32 else ((16, 2) if i8 else (8, 2))
+    steps = -(-wl.I // (8 * V))
+    spw = -(-steps // 4)
+    slice_ = spw * 8 * V * asz
+    R = T * wl.k + wl.S * T
+    lds = 4 * R * slice_ + 4 * R * 8 * 4 + (R * 8 * 4 if i8 else 0) + T * wl.k * 8
+    return spw, slice_, R, lds
+
+
+def down_combine_fits(wl, T):
+    spw, _, _, lds = down_combine_geom(wl, T)
+    max_spw = 6 if wl.wdt == "i8" else 8
+    return 1 <= T and T * 8 <= 256 and T * wl.k <= 256 and spw <= max_spw and lds <= DC_MAX_LDS
+
+
+def routed_inv_perm(wl, T, cap):
+    x = S.make_tokens(wl, T)
+    L = S.make_layer(dataclasses.replace(wl, I=16))  # the router only
+    ids, _ = O.route(O.router_logits(x, L.w_router, L.bias), wl.k, wl.renormalize)
+    return O.permute_with_capacity(ids, wl.E, cap)[3]
+
+
+def check_down_combine(wl, T, offsets, inv_perm, cap):
+    """Every address of k_down_combine in bounds, and the combine reads only rows the ring
+    wrote.  Returns the number of (group, row) sums the blocks form."""
+    K, N = wl.I, wl.d
+    f32, i8 = wl.act == "f32", wl.wdt == "i8"
+    V, asz = (4, 4) if f32 else ((16, 2) if i8 else (8, 2))
+    STEP = 8 * V
+    spw, slice_, R, lds = down_combine_geom(wl, T)
+    assert lds <= DC_MAX_LDS and spw <= 8
+    MAXIT = spw
+    G = wl.E + wl.S
+    Tk = T * wl.k
+    stage_end = 4 * R * slice_
+    part_end = stage_end + 4 * R * 8 * 4
+    scl_end = part_end + (R * 8 * 4 if i8 else 0)
+    assert scl_end + Tk * 8 == lds
+    g, r0, M = touched_groups(wl, T, offsets, cap)
+    nslots = len(g)
+    NG = DC_STREAMS.get(wl.wdt, 2)
+    tid = np.arange(256 * NG)
+    wave, lane = tid // 64, tid % 64
+    q, lg = lane % 8, lane // 8
+    ct, cc = tid // 8, tid % 8
+    steps = -(-K // STEP)
+    # (0) the combine's inputs
+    assert np.all(tid[tid < Tk] < len(inv_perm))
+    written = set()
+    for n0 in range(0, N, 8):
+        n = np.minimum(n0 + lg, N - 1)
+        cn = n0 + cc
+        ridx = np.minimum(ct, T - 1) * N + np.minimum(cn, N - 1)
+        assert np.all((ridx >= 0) & (ridx < T * N))
+        # (1) row staging, the kernel's incremental (row, piece) walk; the NG wavefronts of a
+        #     K-slice take 64 pieces each in turn and together cover every piece once
+        for w in range(4):
+            s_lo = w * spw
+            if s_lo >= steps:
+                continue
+            kw0 = s_lo * STEP
+            cpr = slice_ // 16
+            dr, dp = NG * 64 // cpr, NG * 64 % cpr
+            ln = np.arange(64)
+            covered = np.zeros(R * cpr, dtype=np.int64)
+            for grp in range(NG):
+                r, p = (grp * 64 + ln) // cpr, (grp * 64 + ln) % cpr
+                for c0 in range(grp * 64, R * cpr, NG * 64):
+                    c = c0 + ln
+                    assert np.array_equal(r, c // cpr) and np.array_equal(p, c % cpr)
+                    col = kw0 + p * (16 // asz)
+                    col = np.where(col >= K, kw0, col)
+                    live = r < R
+                    assert np.all(r[live] * K + col[live] + 16 // asz <= R * K)
+                    assert np.all(w * R * slice_ + c0 * 16 + ln[live] * 16 + 16 <= stage_end)
+                    covered[c[live]] += 1
+                    r, p = r + dr, p + dp
+                    wrap = p >= cpr
+                    p, r = np.where(wrap, p - cpr, p), np.where(wrap, r + 1, r)
+            assert np.all(covered == 1)
+        if n0 > 0:
+            continue  # the ring's indexing below does not depend on n0 beyond n (checked)
+        # (2) the weight rings, one per slot stream: issue order, then the rows each group's
+        #     sums cover; every group is taken by exactly one stream
+        issued, taken = [], []
+        for grp in range(NG):
+            mine = -(-(nslots - grp) // NG) if nslots > grp else 0
+            if mine == 0:
+                continue
+            own = [grp + i * NG for i in range(mine)]
+            taken += own
+            issued += [own[min(j, mine - 1)] for j in range(DC_RING)]
+            for i0 in range(0, mine, DC_RING):
+                for j in range(DC_RING):
+                    issued.append(own[min(i0 + j + DC_RING, mine - 1)])
+        assert sorted(taken) == list(range(nslots))
+        for sl in issued:
+            assert 0 <= sl < nslots and 0 <= g[sl] < G
+            for w in range(4):
+                s_lo, s_hi = w * spw, min(steps, w * spw + spw)
+                kw0 = s_lo * STEP
+                for it in range(MAXIT):
+                    col = kw0 + it * STEP + q * V
+                    colc = np.where((s_lo + it < s_hi) & (col < K), col, np.where(q * V < K, q * V, 0))
+                    assert np.all((g[sl] * N + n[lane]) * K + colc + V <= G * N * K)
+                assert np.all(g[sl] * N + n[lane] < G * N)
+        for sl in range(nslots):
+            for w in range(4):
+                s_lo, s_hi = w * spw, min(steps, w * spw + spw)
+                kw0 = s_lo * STEP
+                for m in range(M[sl]):
+                    r = r0[sl] + m
+                    assert r < R
+                    for it in range(MAXIT):
+                        xcol = it * STEP + q * V
+                        ok = (s_lo + it < s_hi) & (kw0 + xcol < K)
+                        rd_bytes = 32 if V == 16 else 16
+                        assert np.all(xcol[ok] * asz + rd_bytes <= slice_)
+                        assert np.all(w * R * slice_ + r * slice_ + xcol[ok] * asz + rd_bytes <= stage_end)
+                    assert stage_end + ((w * R + r) * 8 + 7) * 4 + 4 <= part_end
+                    if i8:
+                        assert part_end + (r * 8 + 7) * 4 + 4 <= scl_end
+                    written.add(int(r))
+    # (3) the combine reads only rows the ring summed; stores stay in y
+    for t in range(T):
+        for j in range(wl.k):
+            r = int(inv_perm[t * wl.k + j])
+            assert r < 0 or r in written, (t, j, r)
+        for s in range(wl.S):
+            assert Tk + s * T + t in written
+    live = (ct < T)[:, None] & ((np.arange(0, N, 8)[None, :] + cc[:, None]) < N)
+    ys = ct[:, None] * N + np.arange(0, N, 8)[None, :] + cc[:, None]
+    assert np.all(ys[live] < T * N)
+    return len(written)
+
+
+DC_CASES = [(S.OLMOE_BF16, 1, 0.0), (S.OLMOE_BF16, 8, 0.0), (S.OLMOE_BF16, 9, 0.0), (S.OLMOE_BF16, 8, 1.0),
+            (S.OLMOE_I8, 1, 0.0), (S.OLMOE_I8, 8, 0.0), (S.OLMOE_I8_ZIPF, 9, 1.0),
+            (S.DEEPSEEK_BF16, 1, 0.0), (S.DEEPSEEK_BF16, 6, 0.0), (S.DEEPSEEK_I8, 4, 0.0),
+            (S.DEEPSEEK_I8, 5, 2.0), (S.TINY_F32, 16, 0.0), (S.TINY_F32, 3, 1.0), (RAGGED16, 7, 0.0),
+            (RAGGED32, 5, 0.0), (WIDE_K, 5, 0.0)]
+
+
+@pytest.mark.parametrize("wl,T,cf", DC_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_down_combine_addresses_stay_in_bounds(wl, T, cf):
+    offsets, perm, cap, _ = routed_plan(wl, T, cf)
+    inv_perm = routed_inv_perm(wl, T, cap)
+    assert down_combine_fits(wl, T)
+    assert check_down_combine(wl, T, offsets, inv_perm, cap) > 0
+
+
+def test_down_combine_limits():
+    """Where the fused launch stops: OLMoE-shaped layers through T=9, DeepSeek-shaped through T=6
+    (the rows' slices fill the 160 KiB of LDS)."""
+    assert down_combine_fits(S.OLMOE_BF16, 9) and not down_combine_fits(S.OLMOE_BF16, 10)
+    assert down_combine_fits(S.OLMOE_I8, 9) and not down_combine_fits(S.OLMOE_I8, 10)
+    assert down_combine_fits(S.DEEPSEEK_BF16, 6) and not down_combine_fits(S.DEEPSEEK_BF16, 7)
+
+
+def test_down_combine_emulation_catches_a_dropped_row():
+    """Not vacuous: a combine that read a dropped row (inv_perm kept at its sorted position
+    past the capacity) is caught."""
+    wl, T = S.OLMOE_BF16, 8
+    offsets, perm, cap, _ = routed_plan(wl, T, 0.25)
+    assert cap > 0
+    full = routed_inv_perm(wl, T, 0)
+    capped = routed_inv_perm(wl, T, cap)
+    assert np.any(capped < 0)
+    with pytest.raises(AssertionError):
+        check_down_combine(wl, T, offsets, full, cap)
