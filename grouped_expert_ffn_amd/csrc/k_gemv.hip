@@ -522,15 +522,17 @@ hipError_t dispatch_gemv_mfma(const GemvArgs& a, int slots, hipStream_t s) {
 //    over the 8 lanes, the fixed-order sum over wavefronts, the int8 scale and the rounding
 //    to the activation type; the sum over a token's rows then follows k_combine's order with
 //    its single rounding.  y is therefore bit-identical to the two launches.
-//  * Each wavefront first stages its own K-slice of all R activation rows into a private LDS
-//    region by direct-to-LDS loads, so no barrier is needed before the end; it waits for all
-//    its loads once, behind the first D groups' weights, before the first sum.
-//  * The weights stream through registers in a ring of D groups: while one group's rows are
-//    summed, the next D-1 groups' loads are in flight.  Every weight load is unconditional
-//    (a lane past its columns reads an in-bounds piece and skips the math), so the number of
-//    loads in flight is a compile-time constant and the compiler's waits leave the ring
-//    running; the ring's tail re-reads the last group D times (a cache hit).
-// grid: ceil(N / 8); block 256; one pass covers K (MAXIT == spw); dynamic LDS from
+//  * The workgroup is NG slot streams of four wavefronts; stream g takes groups g, g + NG, ...
+//    so several groups' weights are in flight per CU.  The wavefronts of one K-slice first
+//    stage that slice of all R activation rows into LDS by direct-to-LDS loads, and one
+//    barrier, behind the first groups' weight loads, makes the rows visible before the first
+//    sum; the next barrier is the one before the combine.
+//  * Each stream's weights pass through registers in a ring of D groups: while one group's
+//    rows are summed, the next D-1 groups' loads are in flight.  Every weight load is
+//    unconditional (a lane past its columns reads an in-bounds piece and skips the math), so
+//    the number of loads in flight is a compile-time constant and the compiler's waits leave
+//    the ring running; the ring's tail re-reads the last group D times (a cache hit).
+// grid: ceil(N / 8); block 256 * NG; one pass covers K (MAXIT == spw); dynamic LDS from
 // down_combine_geom().
 struct DownCombineArgs {
   const void* h;            // [R, K] gate/up output by sorted row
