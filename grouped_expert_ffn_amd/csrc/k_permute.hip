@@ -14,10 +14,11 @@
 // index: the sort is stable and its result unique.
 //
 // Past kSingleMaxRows rows the sort is spread over workgroups of kPermChunk rows each: a
-// first kernel writes every chunk's expert histogram, a scan turns the histograms into each
-// chunk's per-expert base (the rows of that expert in the chunks before it) and the expert
-// totals, and the sort kernel then runs once per chunk (the same offsets the one-workgroup
-// kernel computes, so the result is identical).
+// first kernel writes every chunk's expert histogram; each chunk's per-expert base (the rows
+// of that expert in the chunks before it) and the expert totals come from summing the
+// histograms, inside the sort kernel while there are few chunks, else by a scan launch; the
+// sort kernel then runs once per chunk (the same offsets the one-workgroup kernel computes,
+// so the result is identical).
 //
 // With a capacity limit C, a row whose place in its expert's segment is C or later is
 // dropped (inv_perm = -1): the segment keeps ascending flat order, so these are the pairs
@@ -42,6 +43,7 @@ constexpr int kPermWaves = 16;
 // equal up to 256 rows (OLMoE T=32), where the fused launch saves a launch.
 constexpr int kFusedMaxRows = 256;
 constexpr int kSingleMaxRows = 4096;  // T*k up to which one workgroup sorts every row
+constexpr int kDirectBaseChunks = 64;  // chunks up to which the sort blocks sum their own bases
 constexpr int kStageLoads = kSingleMaxRows / (kPermWaves * kWave);  // staging loads per thread
 static_assert(kFusedMaxRows <= kSingleMaxRows, "the fused kernel sorts in one workgroup");
 static_assert(kPermChunk == kPermWaves * kWave, "one 64-row step per wavefront and chunk");
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
                                                   int32_t* __restrict__ inv_perm,
                                                   int32_t* __restrict__ plan,
                                                   const int32_t* __restrict__ chunk_hist,
-                                                  int cap) {
+                                                  int hist_scanned, int cap) {
   __shared__ int hist[kPermWaves][256];
   __shared__ int pre[kMaxGroups];
   __shared__ int seg[kMaxGroups];  // start of each expert's sorted segment
@@ -132,10 +134,28 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int k, int E, int S, in
       run += c;
     }
     if (multi) {
-      // this chunk's base for each expert and the expert totals (k_perm_scan)
       const int nb = (N + kPermChunk - 1) / kPermChunk;
-      pre[e] = chunk_hist[(size_t)blockIdx.x * E + e];
-      cnt[e] = chunk_hist[(size_t)nb * E + e];
+      if (hist_scanned) {
+        // this chunk's base for each expert and the expert totals (k_perm_scan)
+        pre[e] = chunk_hist[(size_t)blockIdx.x * E + e];
+        cnt[e] = chunk_hist[(size_t)nb * E + e];
+      } else {
+        // few chunks: the rows of expert e in the chunks before this one, and in all of them,
+        // summed here (loads in batches of 8 in flight) instead of by a scan launch
+        int before = 0, total = 0;
+        for (int b0 = 0; b0 < nb; b0 += 8) {
+          int c[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) c[u] = b0 + u < nb ? chunk_hist[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            before += b0 + u < (int)blockIdx.x ? c[u] : 0;
+            total += c[u];
+          }
+        }
+        pre[e] = before;
+        cnt[e] = total;
+      }
     } else {
       pre[e] = 0;
       cnt[e] = run;
@@ -308,17 +328,20 @@ hipError_t launch_permute(const LayerDims& L, int T, const int32_t* ids, int32_t
   }
   if (N <= kSingleMaxRows)
     return launch(MOE_KERNEL_PERMUTE, k_permute<false>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m,
-                  nullptr, 0, nullptr, idsm, counts, offsets, perm, inv_perm, plan, nullptr,
+                  nullptr, 0, nullptr, idsm, counts, offsets, perm, inv_perm, plan, nullptr, 0,
                   capacity_rows(L, T));
-  // three launches: the timer records its start before the first and its stop after the last
-  // launch made while it is alive
+  // two or three launches: the timer records its start before the first and its stop after
+  // the last launch made while it is alive
   LaunchTimer timer(MOE_KERNEL_PERMUTE, s);
   int32_t* chunk_hist = plan + plan_hist_offset(T, L.k, L.E, L.S);
   const int nb = (N + kPermChunk - 1) / kPermChunk;
   k_perm_hist<<<nb, 1024, 0, s>>>(N, L.E, ids, chunk_hist);
-  k_perm_scan<<<(L.E + 255) / 256, 256, 0, s>>>(nb, L.E, chunk_hist);
+  // up to kDirectBaseChunks chunks each sort block sums the histograms before it itself (at
+  // most that many loads per expert); beyond, one scan launch does it once for all blocks
+  const int scanned = nb > kDirectBaseChunks;
+  if (scanned) k_perm_scan<<<(L.E + 255) / 256, 256, 0, s>>>(nb, L.E, chunk_hist);
   k_permute<false><<<nb, 1024, 0, s>>>(T, L.k, L.E, L.S, tile_m, nullptr, 0, nullptr, idsm, counts,
-                                       offsets, perm, inv_perm, plan, chunk_hist,
+                                       offsets, perm, inv_perm, plan, chunk_hist, scanned,
                                        capacity_rows(L, T));
   return hipGetLastError();
 }
@@ -334,7 +357,7 @@ hipError_t launch_topk_permute(const LayerDims& L, int T, const float* logits, i
     return launch(MOE_KERNEL_PERMUTE, k_permute_small, 1, 1024, 0, s, p);
   }
   return launch(MOE_KERNEL_PERMUTE, k_permute<true>, 1, 1024, 0, s, T, L.k, L.E, L.S, tile_m, logits,
-                L.renorm, topk_w, ids, counts, offsets, perm, inv_perm, plan, nullptr,
+                L.renorm, topk_w, ids, counts, offsets, perm, inv_perm, plan, nullptr, 0,
                 capacity_rows(L, T));
 }
 

@@ -214,9 +214,9 @@ typedef enum {
  * `kernel` made by this thread (through any entry point) records start_event and stop_event
  * on that launch's stream, and the hook is then cleared.  A step that is one launch hands
  * the events to the launch itself (hipExtLaunchKernel), so they hold the kernel's own start
- * and end, the window a profiler's kernel trace reports; the multi-workgroup sort (three
- * launches: chunk histograms, their scan, the sort) is bracketed by hipEventRecord before the
- * first and after the last.  Where moe_forward runs the down projection and the combine as
+ * and end, the window a profiler's kernel trace reports; the multi-workgroup sort (chunk
+ * histograms, past 64 chunks their scan, then the sort: two or three launches) is bracketed
+ * by hipEventRecord before the first and after the last.  Where moe_forward runs the down projection and the combine as
  * one launch, MOE_KERNEL_DOWN holds that launch's own window and MOE_KERNEL_COMBINE brackets
  * the same launch.  The events (hipEvent_t) are created and owned by the caller;
  * NULL events disarm the hook.  Returns MOE_ERR_INVALID for an unknown kernel. */

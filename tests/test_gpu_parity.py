@@ -111,12 +111,14 @@ def ids_case(kind, T, E, k, seed):
 
 
 # T*k up to 64 takes the one-wavefront sort (1-64 rows, up to 256 experts and 8 shared),
-# beyond the workgroup sort, past 4096 rows the chunked one
+# beyond the workgroup sort, past 4096 rows the chunked one (chunks of 1024 rows: up to 64
+# chunks the sort blocks sum their own bases, 65528 rows at T=8191; beyond, a scan launch
+# does, 65600 rows at T=8200)
 @pytest.mark.parametrize("T,E,k,S_", [(1, 8, 2, 0), (16, 8, 2, 0), (1, 64, 8, 0), (8, 64, 8, 0),
                                       (10, 64, 6, 2), (64, 8, 1, 0), (9, 256, 7, 8), (37, 64, 6, 2),
                                       (64, 64, 8, 0), (300, 256, 16, 1), (2048, 64, 8, 0),
                                       (2048, 64, 6, 2), (1000, 3, 1, 0), (513, 64, 8, 8),
-                                      (2100, 64, 8, 0)])
+                                      (2100, 64, 8, 0), (8191, 64, 8, 0), (8200, 64, 8, 2)])
 @pytest.mark.parametrize("kind", ["uniform", "same", "zipf"])
 def test_permute_is_bit_exact(T, E, k, S_, kind):
     _permute_case(T, E, k, S_, kind, d=64)

@@ -75,12 +75,13 @@ def test_hook_fires_once():
     assert c.elapsed_time(d) > 0
 
 
-def test_multi_launch_sort_is_bracketed():
-    # T*k past one workgroup's rows: the sort is a histogram launch, a scan and the sort launch,
-    # and the hook brackets all three
+@pytest.mark.parametrize("T", [600, 8300])  # 5 chunks (two launches); 65 chunks (three)
+def test_multi_launch_sort_is_bracketed(T):
+    # T*k past one workgroup's rows: the sort is a histogram launch, past 64 chunks a scan,
+    # and the sort launch, and the hook brackets them all
     from grouped_expert_ffn_amd import abi
     t = C.torch()
-    gl, x = _layer(S.OLMOE_BF16, 600)  # 4800 rows
+    gl, x = _layer(S.OLMOE_BF16, T)
     gl.dev.forward(x)
     t.cuda.synchronize()
     (a, b), (c, d) = _events(t, 2)
