@@ -609,3 +609,27 @@ def test_forward_graph_replay_matches_eager(wl, T):
         gl.dev.forward(x_other)  # eager work on the same workspace between replays
         t.cuda.synchronize()
     del g
+
+
+# In place: y may alias x and the residual may alias either (moe.h).  The same layer run
+# out of place and in place gives the same bits, on the fused decode launch (OLMoE T=1, 8,
+# DeepSeek T=4), the matrix-core GEMV (OLMoE T=64), the GEMM (DeepSeek T=300) and with the
+# RMSNorm prologue.
+INPLACE_CASES = [(S.OLMOE_BF16, 1), (S.OLMOE_BF16, 8), (S.DEEPSEEK_BF16, 4), (S.OLMOE_BF16, 64),
+                 (S.DEEPSEEK_BF16, 300), (S.OLMOE_I8, 8),
+                 (dataclasses.replace(S.OLMOE_BF16, name="olmoe_bf16_prenorm", pre_norm=True), 8)]
+
+
+@pytest.mark.parametrize("wl,T", INPLACE_CASES, ids=case_id)
+def test_forward_in_place_matches_out_of_place(wl, T):
+    from grouped_expert_ffn_amd import to_device
+    t = T_()
+    gl = C.GpuLayer(wl)
+    x = to_device(S.make_tokens(wl, T))
+    ref = gl.dev.forward(x.clone(), residual=x.clone())
+    buf = x.clone()
+    out = gl.dev.forward(buf, residual=buf, y=buf)
+    t.cuda.synchronize()
+    assert out.data_ptr() == buf.data_ptr()
+    assert t.equal(buf, ref)
+    assert not t.equal(buf, x)  # the layer did write its output over the input
