@@ -633,3 +633,20 @@ def test_forward_in_place_matches_out_of_place(wl, T):
     assert out.data_ptr() == buf.data_ptr()
     assert t.equal(buf, ref)
     assert not t.equal(buf, x)  # the layer did write its output over the input
+
+
+@pytest.mark.parametrize("wl,T", [(S.OLMOE_BF16, 8), (S.DEEPSEEK_BF16, 300), (S.TINY_F32, 16)], ids=case_id)
+def test_combine_with_the_residual_in_y(wl, T):
+    # moe_combine's residual may be the output buffer itself
+    from grouped_expert_ffn_amd import moe_combine, to_device
+    t = T_()
+    gl = C.GpuLayer(wl)
+    xd = to_device(S.make_tokens(wl, T))
+    st = C.run_steps(gl, xd, T)
+    res = to_device(S.make_tokens(wl, T, seed=9))
+    ref = t.empty_like(res)
+    moe_combine(gl.desc, T, st["rows"], st["inv_perm"], st["w"], res, ref)
+    buf = res.clone()
+    moe_combine(gl.desc, T, st["rows"], st["inv_perm"], st["w"], buf, buf)
+    t.cuda.synchronize()
+    assert t.equal(buf, ref)
