@@ -15,11 +15,21 @@ same workload, and compares its outputs with the GPU's for the headline tokens.
 
 The expert weights are replicated ``--copies`` times and the steps rotate over
 the copies, so the 256 MiB Infinity Cache cannot serve the weights of the next
-step (``copies_plateau`` shows the time no longer falls with more copies).  The
-dominant kernel (grouped gate/up) is additionally timed per launch with HIP
-events through the library's one-shot timing hook, for the roofline.  The same
-steps are also captured once in a HIP graph and replayed (checked bit for bit
-against the eager result first).
+step (``copies_plateau`` shows the time no longer falls with more copies).
+
+Timed steps run inside one HIP graph: the K timed forwards (rotating over the
+weight copies) are captured once into a single graph, which is replayed three
+times with the output cleared, eager work and a synchronisation in between and
+must reproduce the eager output bit for bit; the timed region is then one
+replay of the K steps, after the warm-up steps.  Launched this way, no step
+waits on the host: eager launches fetch their kernel arguments from host memory
+on machines whose runtime keeps them there (about 1.1 us per launch, four or
+five launches per layer), and a graph of one forward per replay pays about 5 us
+of launch latency per replay.  The eager time is reported beside the graph time
+(``eager_ms_per_layer``).  The dominant kernel (grouped gate/up) is
+additionally timed per launch with HIP events through the library's one-shot
+timing hook (eager launches; the events bracket the kernel itself), for the
+roofline.
 
 After the headline, the other workload points are timed (``--sweep``; each the
 median of three windows of at least 5 ms of steps), then the 16-layer prefill stack (RMSNorm + MoE + residual per layer, T=2048, Zipf
@@ -74,7 +84,7 @@ def parse():
                    help="workload:T@capacity_factor points with token dropping ('' or none for none)")
     p.add_argument("--stack-steps", type=int, default=5, help="timed passes over the 16 layers")
     p.add_argument("--no-extras", action="store_true",
-                   help="skip graph replay, copies plateau and copy ceiling")
+                   help="skip the step percentiles, copies plateau and copy ceiling")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--counters-pass", action="store_true",
@@ -174,7 +184,7 @@ def time_steps_median(step, steps, per_step_ms, windows=3, min_window_ms=5.0):
     """The sweep and capacity points: the median of `windows` timed windows, each of at least
     `steps` steps and `min_window_ms` of GPU work, so that one slow step in a short window
     (a decode layer takes 30 µs) does not move the point."""
-    n = max(steps, int(min_window_ms / max(per_step_ms, 1e-3)) + 1)
+    n = window_steps(steps, per_step_ms, min_window_ms)
     runs = sorted(time_steps(step, n, 0) for _ in range(windows))
     return runs[len(runs) // 2]
 
@@ -209,31 +219,57 @@ def time_kernel(kernel, launch, launches):
     return sum(ds) / len(ds), min(ds)
 
 
-def graph_replay(capture_calls, y, reference, replays):
-    """Capture `capture_calls(stream)` once in a HIP graph, check that replays reproduce
-    `reference` bit for bit (with eager work and synchronisations in between), then time
-    `replays` replays.  Returns ms per replay."""
+def capture_graphs(captures, y, reference, checks=3):
+    """One HIP graph per entry of `captures` (each `capture(stream)` records its launches on
+    the capture stream it is handed).  Every graph is replayed `checks` times, with `y`
+    cleared, eager work and a synchronisation between replays, and must reproduce
+    `reference` bit for bit, else the point is refused.  Returns the graphs."""
     import torch
-    g = torch.cuda.CUDAGraph()
+    graphs = []
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        capture_calls(torch.cuda.current_stream().cuda_stream)
-    for _ in range(3):
-        y.zero_()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(y, reference):
-            raise SystemExit("graph replay differs from the eager result; refusing to time it")
+    for capture in captures:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            capture(torch.cuda.current_stream().cuda_stream)
+        graphs.append(g)
+    for g in graphs:
+        for _ in range(checks):
+            y.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(y, reference):
+                raise SystemExit("graph replay differs from the eager result; refusing to time it")
+    return graphs
+
+
+def time_graph(g, n_steps, warm=None, warmup=0):
+    """ms of one step when one replay of `g` runs `n_steps` steps, after `warmup` untimed
+    calls of `warm(i)`; the replay is bracketed by synchronisations."""
+    import torch
+    for i in range(warmup):
+        warm(i)
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     ev0.record()
-    for _ in range(replays):
-        g.replay()
+    g.replay()
     ev1.record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / replays
-    del g
-    return ms
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / n_steps, wall
+
+
+def time_graph_median(g, n_steps, windows=3):
+    """The median of `windows` replays (each `n_steps` steps), as ms per step."""
+    runs = sorted(time_graph(g, n_steps) for _ in range(windows))
+    return runs[len(runs) // 2]
+
+
+def window_steps(steps, per_step_ms, min_window_ms=5.0):
+    """Steps in a timed window of a sweep or capacity point: at least `steps` and at least
+    `min_window_ms` of GPU work."""
+    return max(steps, int(min_window_ms / max(per_step_ms, 1e-3)) + 1)
 
 
 def copy_ceiling_gbs(mib=1024, reps=10):
@@ -383,21 +419,25 @@ class Point:
         self.y_host, self.ids_host = y1, ids
         return ids
 
-    def graph_ms(self, replays):
-        """One graph holds one forward per weight copy; ms per layer of a replay."""
+    def graph_of(self, n):
+        """`n` forwards, step i on weight copy i % copies, captured in one graph and checked
+        against the eager output."""
         import torch
         for i in range(len(self.args)):
             self.step(i)
         torch.cuda.synchronize()
         ref = self.y.clone()
+        lib, args_for, layers = self.lib, self.args_for, self.layers
 
         def capture(stream):
-            for L in self.layers:
-                _call(self.lib, self.args_for(L, stream))
-        return graph_replay(capture, self.y, ref, replays) / len(self.layers)
+            for i in range(n):
+                _call(lib, args_for(layers[i % len(layers)], stream))
+        self.graphs = capture_graphs([capture], self.y, ref)
+        return self.graphs[0]
 
     def free(self):
         import torch
+        self.graphs = None
         self.layers.clear()
         self.args.clear()
         torch.cuda.empty_cache()
@@ -445,9 +485,12 @@ def measure(wl, T, steps, warmup, copies, extras=False):
     work = layer_work(wl, T, n_touched)
     if warmup is None:  # a sweep point
         _, per_step = warm_up(pt.step, copies)
-        ms, wall = time_steps_median(pt.step, steps, per_step)
+        n = window_steps(steps, per_step)
+        ms, wall = time_graph_median(pt.graph_of(n), n)
+        eager_ms, _ = time_steps_median(pt.step, steps, per_step)
     else:
-        ms, wall = time_steps(pt.step, steps, warmup)
+        ms, wall = time_graph(pt.graph_of(steps), steps, pt.step, warmup)
+        eager_ms, _ = time_steps(pt.step, steps, warmup)
     launches = 50  # the average over 50 launches, as rocprofv3's kernel statistics report it
     gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, pt.step, launches)
     dn_ms, _ = time_kernel(abi.MOE_KERNEL_DOWN, pt.step, launches)
@@ -460,14 +503,14 @@ def measure(wl, T, steps, warmup, copies, extras=False):
         "gate_up_hbm_frac": round(work["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "down_hbm_frac": round(work["down_bytes"] / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "touched_experts": n_touched,
+        "eager_ms_per_layer": round(eager_ms, 5),
         "oracle_gate": gate,
     }
     if T > 8 and wl.act == "bf16":
         res["gate_up_mfma_frac"] = round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
         res["down_mfma_frac"] = round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
     if extras:
-        res["step_ms_percentiles"] = step_percentiles(pt.step, steps)
-        res["graph_ms_per_layer"] = round(pt.graph_ms(max(4, steps // copies)), 5)
+        res["eager_step_ms_percentiles"] = step_percentiles(pt.step, steps)
     roof = roofline_for(wl, T, work, gu_ms)
     # the whole layer (every launch of the step) against the same HBM peak, beside the one
     # kernel's fraction: at small T the fixed cost of the other launches is what separates them
@@ -484,7 +527,7 @@ def copies_plateau(wl, T, counts=(1, 2, 4, 8, 16), steps=32):
     out = {}
     for n in counts:
         pt = Point(wl, T, n)
-        ms, _ = time_steps(pt.step, steps, 4)
+        ms, _ = time_graph(pt.graph_of(steps), steps, pt.step, 4)
         out[str(n)] = round(ms, 5)
         pt.free()
     return out
@@ -529,6 +572,23 @@ class Stack:
     def layer(self, i):
         _call(self.lib, self.args[i % len(self.args)])
 
+    def graph_of(self, passes):
+        """`passes` whole passes captured in one graph, checked against the eager pass."""
+        import torch
+        self.step()
+        torch.cuda.synchronize()
+        out = self.buf[(len(self.layers) - 1) % 2]
+        ref = out.clone()
+
+        def capture(stream):
+            for _ in range(passes):
+                for i, L in enumerate(self.layers):
+                    src = self.x0 if i == 0 else self.buf[(i - 1) % 2]
+                    _call(self.lib, _forward_args(self.desc, self.T, src, L, src, self.buf[i % 2],
+                                                  self.ws, stream))
+        self.graphs = capture_graphs([capture], out, ref)
+        return self.graphs[0]
+
     def sanity_gate(self):
         """Layer 0 twice: the output must be finite and bit-identical; records the busiest
         expert's load over the mean."""
@@ -552,6 +612,7 @@ class Stack:
 
     def free(self):
         import torch
+        self.graphs = None
         self.layers.clear()
         self.args.clear()
         self.host0 = None
@@ -564,7 +625,8 @@ def measure_stack(wl, steps):
     st.sanity_gate()
     T, n = st.T, wl.n_layers
     warm_up(st.step, 1)
-    ms, _ = time_steps(st.step, steps, 0)
+    ms, _ = time_graph(st.graph_of(steps), steps)
+    eager_ms, _ = time_steps(st.step, steps, 0)
     gu_ms, _ = time_kernel(abi.MOE_KERNEL_GATE_UP, st.layer, 2 * n)
     dn_ms, _ = time_kernel(abi.MOE_KERNEL_DOWN, st.layer, 2 * n)
     work = layer_work(wl, T, wl.E)  # every expert is touched at T=2048
@@ -577,6 +639,7 @@ def measure_stack(wl, steps):
         "gate_up_ms": round(gu_ms, 5), "down_ms": round(dn_ms, 5),
         "gate_up_mfma_frac": round(work["gate_up_flops"] / (gu_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "down_mfma_frac": round(work["down_flops"] / (dn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "eager_ms_per_stack": round(eager_ms, 4),
         "busiest_over_mean_layer0": round(st.skew0, 3),
         "oracle_gate_layer0": st.gate,
     }
@@ -608,11 +671,14 @@ def measure_capacity(wl, T, cf, steps, copies):
     cap, dropped = drop_stats(ids, wl.E, cf)
     gate = capacity_gate(wl, pt, ids, cf, dropped)
     _, per_step = warm_up(pt.step, copies)
-    ms, _ = time_steps_median(pt.step, steps, per_step)
+    n = window_steps(steps, per_step)
+    ms, _ = time_graph_median(pt.graph_of(n), n)
+    eager_ms, _ = time_steps_median(pt.step, steps, per_step)
     pt.free()
     counts = np.bincount(ids.ravel(), minlength=wl.E)
     return {"workload": wl.name, "tokens": T, "capacity_factor": cf, "capacity_rows": cap,
             "ms_per_layer": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "eager_ms_per_layer": round(eager_ms, 5),
             "dropped_pairs_frac": round(float(dropped.mean()), 4),
             "tokens_with_a_drop_frac": round(float(dropped.any(axis=1).mean()), 4),
             "busiest_over_mean": round(float(counts.max() / (T * wl.k / wl.E)), 3),

@@ -611,6 +611,44 @@ def test_forward_graph_replay_matches_eager(wl, T):
     del g
 
 
+# Several forwards in one graph, alternating two weight copies and two token batches over one
+# shared workspace (the form bench.py times): every output equals its eager result bit for bit
+# on each replay.
+@pytest.mark.parametrize("wl,T", [(S.OLMOE_BF16, 8), (S.OLMOE_BF16, 1), (S.DEEPSEEK_BF16, 300)],
+                         ids=case_id)
+def test_graph_of_several_forwards_matches_eager(wl, T):
+    from grouped_expert_ffn_amd import DeviceLayer, abi, to_device
+    t = T_()
+    gl = C.GpuLayer(wl)
+    d = gl.dev
+    twin = DeviceLayer(gl.desc, d.w_router, d.bias, d.w_gate.clone(), d.w_up.clone(), d.w_down.clone(),
+                       None if d.s_gate is None else d.s_gate.clone(),
+                       None if d.s_up is None else d.s_up.clone(),
+                       None if d.s_down is None else d.s_down.clone())
+    xs = [to_device(S.make_tokens(wl, T, seed=s)) for s in (0, 7)]
+    eager = [d.forward(x) for x in xs]
+    t.cuda.synchronize()
+    ws = d.workspace(T)
+    ys = [t.empty_like(e) for e in eager]
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        for i in range(6):
+            L = (d, twin)[i % 2]
+            abi.moe_forward(gl.desc, T, xs[(i // 2) % 2], L.w_router, L.bias, L.weights, None,
+                            ys[(i // 2) % 2], None, None, ws, ws.numel())
+    for _ in range(3):
+        for y in ys:
+            y.zero_()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert t.equal(y, e)
+        d.forward(xs[1])  # eager work on the same workspace between replays
+        t.cuda.synchronize()
+    del g
+
+
 # In place: y may alias x and the residual may alias either (moe.h).  The same layer run
 # out of place and in place gives the same bits, on the fused decode launch (OLMoE T=1, 8,
 # DeepSeek T=4), the matrix-core GEMV (OLMoE T=64), the GEMM (DeepSeek T=300) and with the
