@@ -521,13 +521,14 @@ def measure(wl, T, steps, warmup, copies, extras=False):
     return res, roof, ms, wall, work, checked
 
 
-def copies_plateau(wl, T, counts=(1, 2, 4, 8, 16), steps=32):
+def copies_plateau(wl, T, counts=(1, 2, 4, 8, 16), steps=50):
     """Layer time against the number of weight copies rotated over: it falls while the
-    Infinity Cache still holds the next step's weights, then stays flat."""
+    Infinity Cache still holds the next step's weights, then stays flat.  Timed like the
+    headline (warm-up of at least two rotations and 16 steps, then one graph of the steps)."""
     out = {}
     for n in counts:
         pt = Point(wl, T, n)
-        ms, _ = time_graph(pt.graph_of(steps), steps, pt.step, 4)
+        ms, _ = time_graph(pt.graph_of(steps), steps, pt.step, max(16, 2 * n))
         out[str(n)] = round(ms, 5)
         pt.free()
     return out
