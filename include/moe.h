@@ -1,7 +1,7 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) MoE token-dispatch library, libmoe.so.
  *
- * One Mixture-of-Experts layer on one GPU, in four steps and one call for all of them:
+ * One Mixture-of-Experts layer on one GPU: five steps in four calls, and one call for all:
  *   moe_route        router GEMM, softmax over all experts, top-k, optional renormalisation
  *   moe_permute      stable sort of the (token, slot) rows by expert: counts, offsets,
  *                    perm, inv_perm, plus the launch plan of the grouped FFN
